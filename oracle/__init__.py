@@ -1,0 +1,156 @@
+"""CPU oracle for single-token decode attention (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg import
+this package. It wraps ``liboracle.so``, built from ``ada_oracle.c`` with the
+host C compiler, through ctypes. It shares no code with the GPU library and
+imports nothing from it.
+
+The C source states the definition it computes and the page sections it
+follows. Every function is pinned by ``tests/test_oracle_pins.py`` to results
+obtained another way (an independent library attention routine, closed forms,
+invariants, exhaustive decoder checks), and ``tests/test_oracle_mutants.py``
+shows that plausible mistakes in the source fail those pins.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import tempfile
+from pathlib import Path
+
+import numpy as np
+
+ORACLE_DIR = Path(__file__).resolve().parent
+SOURCE = ORACLE_DIR / "ada_oracle.c"
+LIBRARY = ORACLE_DIR / "liboracle.so"
+
+DTYPES = {"fp16": 0, "bf16": 1}
+
+
+def build(source: Path | str = SOURCE, output: Path | str = LIBRARY, openmp: bool = True) -> Path:
+    """Compile the oracle into a shared library with the host C compiler."""
+    output = Path(output)
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra"]
+    if openmp:
+        cmd.append("-fopenmp")
+    cmd += ["-o", str(output) + ".tmp", str(source), "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(str(output) + ".tmp", output)
+    return output
+
+
+def build_from_text(text: str, directory: str | None = None) -> Path:
+    """Compile oracle source given as text (used by the mutation tests)."""
+    d = Path(directory or tempfile.mkdtemp(prefix="ada_oracle_"))
+    src = d / "ada_oracle_variant.c"
+    src.write_text(text)
+    return build(src, d / "liboracle_variant.so", openmp=False)
+
+
+def _bits(x) -> np.ndarray:
+    """Raw 16-bit patterns of a torch fp16/bf16 tensor or a uint16 array."""
+    if isinstance(x, np.ndarray):
+        if x.dtype != np.uint16:
+            raise TypeError("numpy inputs must hold raw uint16 bit patterns")
+        return np.ascontiguousarray(x)
+    import torch
+
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError(f"expected a 16-bit float tensor, got {x.dtype}")
+    return x.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _dtype_name(x, dtype: str | None) -> str:
+    if dtype is not None:
+        return dtype
+    import torch
+
+    return {torch.float16: "fp16", torch.bfloat16: "bf16"}[x.dtype]
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+class Oracle:
+    """ctypes view of one build of the oracle library."""
+
+    def __init__(self, path: Path | str = LIBRARY):
+        self.path = Path(path)
+        lib = ctypes.CDLL(str(self.path))
+        u16p = ctypes.POINTER(ctypes.c_uint16)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        c_int = ctypes.c_int
+        lib.ada_oracle_decode.argtypes = [u16p, u16p, u16p, i32p, c_int, c_int, c_int, c_int, c_int,
+                                          ctypes.c_double, c_int, f64p]
+        lib.ada_oracle_decode.restype = c_int
+        lib.ada_oracle_kv_append.argtypes = [u16p, u16p, u16p, u16p, i32p, c_int, c_int, c_int, c_int]
+        lib.ada_oracle_kv_append.restype = c_int
+        lib.ada_oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.ada_oracle_f16_to_f64.restype = ctypes.c_double
+        lib.ada_oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+        lib.ada_oracle_bf16_to_f64.restype = ctypes.c_double
+        lib.ada_oracle_threads.argtypes = []
+        lib.ada_oracle_threads.restype = c_int
+        self._lib = lib
+
+    def threads(self) -> int:
+        return int(self._lib.ada_oracle_threads())
+
+    def decode_bits(self, bits: np.ndarray, dtype: str) -> np.ndarray:
+        """Decode an array of raw 16-bit patterns to float64, one by one."""
+        fn = self._lib.ada_oracle_bf16_to_f64 if dtype == "bf16" else self._lib.ada_oracle_f16_to_f64
+        flat = np.asarray(bits, dtype=np.uint16).ravel()
+        return np.array([fn(int(b)) for b in flat], dtype=np.float64).reshape(np.shape(bits))
+
+    def decode(self, q, k_cache, v_cache, kv_len, scale: float, dtype: str | None = None) -> np.ndarray:
+        """out[b, h, :] in float64 for q [B, Hq, D], caches [B, Hkv, S, D]."""
+        dt = _dtype_name(q, dtype)
+        qb, kb, vb = _bits(q), _bits(k_cache), _bits(v_cache)
+        if qb.ndim == 4:  # [B, Hq, 1, D]
+            qb = qb.reshape(qb.shape[0], qb.shape[1], qb.shape[3])
+        batch, n_head, head_dim = qb.shape
+        kb_, n_kv_head, capacity, kd = kb.shape
+        if kb.shape != vb.shape or kb_ != batch or kd != head_dim:
+            raise ValueError("inconsistent shapes")
+        lens = np.ascontiguousarray(np.asarray(
+            kv_len.cpu().numpy() if hasattr(kv_len, "cpu") else kv_len, dtype=np.int32).reshape(batch))
+        out = np.zeros((batch, n_head, head_dim), dtype=np.float64)
+        rc = self._lib.ada_oracle_decode(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16),
+                                         _ptr(vb, ctypes.c_uint16), _ptr(lens, ctypes.c_int32),
+                                         batch, n_head, n_kv_head, head_dim, capacity,
+                                         float(scale), DTYPES[dt], _ptr(out, ctypes.c_double))
+        if rc != 0:
+            raise ValueError(f"oracle decode failed with status {rc}")
+        return out
+
+    def kv_append(self, k_new, v_new, k_cache, v_cache, pos):
+        """Return updated copies of the caches (inputs are not modified)."""
+        kn, vn = _bits(k_new), _bits(v_new)
+        kc, vc = _bits(k_cache).copy(), _bits(v_cache).copy()
+        batch, n_kv_head, capacity, head_dim = kc.shape
+        p = np.ascontiguousarray(np.asarray(
+            pos.cpu().numpy() if hasattr(pos, "cpu") else pos, dtype=np.int32).reshape(batch))
+        kn = np.ascontiguousarray(kn.reshape(batch, n_kv_head, head_dim))
+        vn = np.ascontiguousarray(vn.reshape(batch, n_kv_head, head_dim))
+        rc = self._lib.ada_oracle_kv_append(_ptr(kn, ctypes.c_uint16), _ptr(vn, ctypes.c_uint16),
+                                            _ptr(kc, ctypes.c_uint16), _ptr(vc, ctypes.c_uint16),
+                                            _ptr(p, ctypes.c_int32), batch, n_kv_head, capacity, head_dim)
+        if rc != 0:
+            raise ValueError(f"oracle kv_append failed with status {rc}")
+        return kc, vc
+
+
+_DEFAULT: Oracle | None = None
+
+
+def load() -> Oracle:
+    """The oracle built from ``ada_oracle.c``; compiled here if not yet built."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        if not LIBRARY.exists() or LIBRARY.stat().st_mtime < SOURCE.stat().st_mtime:
+            build()
+        _DEFAULT = Oracle(LIBRARY)
+    return _DEFAULT
