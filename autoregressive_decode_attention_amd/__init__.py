@@ -1,0 +1,339 @@
+"""Single-token decode attention for AMD MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libada.so``, whose C ABI is declared in
+``include/ada.h``. Every step of the computation runs in the library's HIP
+kernels; this module only checks tensors, takes their device pointers and the
+current HIP stream, and manages a cached split workspace. PyTorch is used for
+device memory and streams only.
+
+The functions keep the C names without the ``ada_`` prefix:
+
+* ``kv_append(k_new, v_new, k_cache, v_cache, pos)``
+* ``decode_attn_gqa(q, k_cache, v_cache, kv_len, scale=None, out=None, max_kv_len=None)``
+* ``decode_attn_gqa_ex(..., num_splits=...)``
+* ``decode_partial(q, k_cache, v_cache, kv_len, ...)`` and
+  ``decode_combine(workspace, num_splits, out, n_kv_head)``: the two halves
+* ``decode_num_splits``, ``decode_workspace_bytes``, ``device_num_cus``,
+ , ``status_string``, ``last_hip_error``, ``abi_version``.
+
+There is no fallback: if the library is missing, importing this package
+raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from pathlib import Path
+
+import torch  # loads the HIP runtime the library then shares
+
+PKG_DIR = Path(__file__).resolve().parent
+LIB_PATH = PKG_DIR / "libada.so"
+
+F16, BF16 = 0, 1
+_DTYPE_CODES = {torch.float16: F16, torch.bfloat16: BF16}
+HEAD_DIM = 128
+MAX_SPLITS = 256
+
+STATUS = {
+    0: "ADA_OK", -1: "ADA_ERR_NULL", -2: "ADA_ERR_SHAPE", -3: "ADA_ERR_GQA", -4: "ADA_ERR_DTYPE",
+    -5: "ADA_ERR_HEAD_DIM", -6: "ADA_ERR_SCALE", -7: "ADA_ERR_WORKSPACE", -8: "ADA_ERR_SPLITS",
+    -9: "ADA_ERR_ALIGN", -10: "ADA_ERR_HIP",
+}
+
+EXPORTS = (
+    "ada_abi_version", "ada_status_string", "ada_last_hip_error", "ada_device_num_cus",
+    "ada_kv_append", "ada_decode_num_splits", "ada_decode_workspace_bytes",
+    "ada_decode_attn_gqa", "ada_decode_attn_gqa_ex", "ada_decode_partial", "ada_decode_combine",
+)
+
+
+class AdaError(RuntimeError):
+    """A libada call returned a non-zero status."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {STATUS.get(status, status)} ({_status_text(status)})"
+        if status == -10:
+            msg += f", hipError {last_hip_error()}"
+        super().__init__(msg)
+
+
+def _declare(lib):
+    c_int, c_void_p, c_size_t, c_float = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_float
+    decode_args = [c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
+                   c_float, c_int, c_void_p, c_void_p, c_size_t, c_void_p]
+    sigs = {
+        "ada_abi_version": ([], c_int),
+        "ada_status_string": ([c_int], ctypes.c_char_p),
+        "ada_last_hip_error": ([], c_int),
+        "ada_device_num_cus": ([c_int, ctypes.POINTER(c_int)], c_int),
+        "ada_kv_append": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
+                           c_int, c_void_p], c_int),
+        "ada_decode_num_splits": ([c_int, c_int, c_int, c_int], c_int),
+        "ada_decode_workspace_bytes": ([c_int, c_int, c_int, c_int, c_int], c_size_t),
+        "ada_decode_attn_gqa": (decode_args, c_int),
+        "ada_decode_attn_gqa_ex": (decode_args + [c_int], c_int),
+        "ada_decode_partial": ([c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
+                                c_float, c_int, c_int, c_void_p, c_size_t, ctypes.POINTER(c_int), c_void_p], c_int),
+        "ada_decode_combine": ([c_void_p, c_size_t, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p],
+                               c_int),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+def load_library(path: Path | str = LIB_PATH):
+    """Load a build of libada and declare its C signatures."""
+    path = Path(path)
+    if not path.exists():
+        raise ImportError(f"{path} is not built; run `python autoregressive_decode_attention_amd/build.py` "
+                          "(or __graft_entry__.build()) first")
+    return _declare(ctypes.CDLL(str(path)))
+
+
+_lib = load_library()
+
+
+def _status_text(status: int) -> str:
+    return _lib.ada_status_string(int(status)).decode()
+
+
+def status_string(status: int) -> str:
+    return _status_text(status)
+
+
+def last_hip_error() -> int:
+    return int(_lib.ada_last_hip_error())
+
+
+def abi_version() -> int:
+    return int(_lib.ada_abi_version())
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise AdaError(status, where)
+
+
+def device_num_cus(device=None) -> int:
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    n = ctypes.c_int(0)
+    _check(_lib.ada_device_num_cus(dev.index if dev.index is not None else torch.cuda.current_device(),
+                                   ctypes.byref(n)), "ada_device_num_cus")
+    return n.value
+
+
+_CUS: dict = {}
+
+
+def _cus(device: torch.device) -> int:
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    if idx not in _CUS:
+        _CUS[idx] = device_num_cus(torch.device("cuda", idx))
+    return _CUS[idx]
+
+
+def decode_num_splits(batch: int, n_kv_head: int, max_kv_len: int, num_cus: int | None = None) -> int:
+    if num_cus is None:
+        num_cus = _cus(torch.device("cuda", torch.cuda.current_device()))
+    return int(_lib.ada_decode_num_splits(int(batch), int(n_kv_head), int(max_kv_len), int(num_cus)))
+
+
+def decode_workspace_bytes(batch: int, n_head: int, n_kv_head: int, head_dim: int, num_splits: int) -> int:
+    return int(_lib.ada_decode_workspace_bytes(int(batch), int(n_head), int(n_kv_head), int(head_dim),
+                                               int(num_splits)))
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A workspace of ``nbytes`` bytes on ``device`` (scratch; needs no preparation)."""
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# Cached workspaces, one per (device, stream): calls on one stream are ordered.
+_WORKSPACES: dict = {}
+
+
+def _workspace(device: torch.device, nbytes: int) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    key = (device.index, _stream(device))
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = new_workspace(max(nbytes, 2 * (ws.numel() if ws is not None else 0)), device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr() if t is not None else 0)
+
+
+def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+              pos) -> None:
+    """Write k_new/v_new [B, Hkv, D] (or [B, Hkv, 1, D]) into slot pos[b] of the
+    caches [B, Hkv, S, D], in place, on the current stream. ``pos``: int32
+    device tensor [B], or host ints (copied to the device)."""
+    _require(k_cache.is_cuda and k_cache.dim() == 4, "k_cache must be a 4-d GPU tensor [B, Hkv, S, D]")
+    B, Hkv, S, D = k_cache.shape
+    _require(v_cache.shape == k_cache.shape, "v_cache shape must equal k_cache shape")
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _require(t.dtype == k_cache.dtype and t.device == k_cache.device and t.is_contiguous(),
+                 f"{name} must be contiguous, on {k_cache.device}, dtype {k_cache.dtype}")
+    _require(k_new.numel() == B * Hkv * D and v_new.numel() == B * Hkv * D, "k_new/v_new must be [B, Hkv, D]")
+    _require(k_cache.dtype in _DTYPE_CODES, "dtype must be float16 or bfloat16")
+    pos_t = _as_int32(pos, B, k_cache.device)
+    _check(_lib.ada_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(pos_t), B, Hkv, S, D,
+                              _DTYPE_CODES[k_cache.dtype], ctypes.c_void_p(_stream(k_cache.device))),
+           "ada_kv_append")
+
+
+def _as_int32(x, batch: int, device) -> torch.Tensor:
+    if isinstance(x, torch.Tensor):
+        _require(x.dtype == torch.int32 and x.is_cuda and x.is_contiguous() and x.numel() == batch,
+                 "index tensors must be contiguous int32 GPU tensors with one entry per batch row")
+        return x
+    vals = [int(v) for v in (x if hasattr(x, "__len__") else [x] * batch)]
+    _require(len(vals) == batch, "need one entry per batch row")
+    return torch.tensor(vals, dtype=torch.int32, device=device)
+
+
+def decode_attn_gqa_ex(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len,
+                       scale: float | None = None, out: torch.Tensor | None = None,
+                       max_kv_len: int | None = None, num_splits: int = 0,
+                       workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode attention with a forced split count (0 = heuristic)."""
+    _require(k_cache.is_cuda and k_cache.dim() == 4, "k_cache must be a 4-d GPU tensor [B, Hkv, S, D]")
+    B, Hkv, S, D = k_cache.shape
+    _require(v_cache.shape == k_cache.shape, "v_cache shape must equal k_cache shape")
+    _require(q.dim() in (3, 4) and q.shape[0] == B and q.shape[-1] == D and (q.dim() == 3 or q.shape[2] == 1),
+             "q must be [B, Hq, D] or [B, Hq, 1, D]")
+    Hq = q.shape[1]
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _require(t.dtype == k_cache.dtype and t.device == k_cache.device and t.is_contiguous(),
+                 f"{name} must be contiguous, on {k_cache.device}, dtype {k_cache.dtype}")
+    _require(k_cache.dtype in _DTYPE_CODES, "dtype must be float16 or bfloat16")
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out.shape == q.shape and out.dtype == q.dtype and out.device == q.device and out.is_contiguous(),
+             "out must be a contiguous tensor like q")
+    if isinstance(kv_len, torch.Tensor):
+        lens_t = _as_int32(kv_len, B, k_cache.device)
+        mkl = S if max_kv_len is None else int(max_kv_len)
+    else:
+        host = [int(v) for v in (kv_len if hasattr(kv_len, "__len__") else [kv_len] * B)]
+        lens_t = _as_int32(host, B, k_cache.device)
+        mkl = max(1, min(S, max(host) if host else 1)) if max_kv_len is None else int(max_kv_len)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    plan_len = S if mkl <= 0 else min(mkl, S)  # the library reads max_kv_len <= 0 as the capacity
+    if num_splits > 0:
+        chunk = -(-plan_len // num_splits)
+        splits = -(-plan_len // chunk)
+    else:
+        splits = decode_num_splits(B, Hkv, plan_len)
+    need = decode_workspace_bytes(B, Hq, Hkv, D, splits) if splits > 1 else 0
+    ws = workspace if workspace is not None else _workspace(k_cache.device, need)
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    rc = _lib.ada_decode_attn_gqa_ex(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens_t), B, Hq, Hkv, D, S, mkl,
+                                     ctypes.c_float(scale), _DTYPE_CODES[k_cache.dtype], _ptr(out), _ptr(ws),
+                                     ws_bytes, ctypes.c_void_p(_stream(k_cache.device)), int(num_splits))
+    _check(rc, "ada_decode_attn_gqa_ex")
+    return out
+
+
+def _check_decode_inputs(q, k_cache, v_cache):
+    _require(k_cache.is_cuda and k_cache.dim() == 4, "k_cache must be a 4-d GPU tensor [B, Hkv, S, D]")
+    B, Hkv, S, D = k_cache.shape
+    _require(v_cache.shape == k_cache.shape, "v_cache shape must equal k_cache shape")
+    _require(q.dim() in (3, 4) and q.shape[0] == B and q.shape[-1] == D and (q.dim() == 3 or q.shape[2] == 1),
+             "q must be [B, Hq, D] or [B, Hq, 1, D]")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _require(t.dtype == k_cache.dtype and t.device == k_cache.device and t.is_contiguous(),
+                 f"{name} must be contiguous, on {k_cache.device}, dtype {k_cache.dtype}")
+    _require(k_cache.dtype in _DTYPE_CODES, "dtype must be float16 or bfloat16")
+    return B, q.shape[1], Hkv, S, D
+
+
+def workspace_layout(batch: int, n_head: int, num_splits: int, head_dim: int = HEAD_DIM) -> dict:
+    """Byte offsets of the split-major partials in a workspace (as include/ada.h
+    documents them): float2 (m, l) per (split, batch row, query head) from
+    ``ml_offset``, float[head_dim] accumulators from ``acc_offset``."""
+    r256 = lambda x: (x + 255) // 256 * 256
+    rows = batch * n_head * num_splits
+    acc_offset = r256(rows * 8)
+    return {"ml_offset": 0, "acc_offset": acc_offset, "total": acc_offset + r256(rows * head_dim * 4),
+            "rows_per_split": batch * n_head}
+
+
+def decode_partial(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len,
+                   scale: float | None = None, max_kv_len: int | None = None, num_splits: int = 0,
+                   workspace: torch.Tensor | None = None):
+    """First half of a decode call: per-split partial results (running max, sum
+    and unnormalised accumulator, split-major) written to ``workspace``.
+    Returns ``(workspace, splits_used)``."""
+    B, Hq, Hkv, S, D = _check_decode_inputs(q, k_cache, v_cache)
+    lens_t = _as_int32(kv_len, B, k_cache.device) if isinstance(kv_len, torch.Tensor) else \
+        _as_int32([int(v) for v in (kv_len if hasattr(kv_len, "__len__") else [kv_len] * B)], B, k_cache.device)
+    mkl = S if max_kv_len is None else int(max_kv_len)
+    plan_len = S if mkl <= 0 else min(mkl, S)
+    if num_splits > 0:
+        chunk = -(-plan_len // num_splits)
+        splits = -(-plan_len // chunk)
+    else:
+        splits = decode_num_splits(B, Hkv, plan_len)
+    if workspace is None:
+        workspace = new_workspace(decode_workspace_bytes(B, Hq, Hkv, D, splits), k_cache.device)
+    used = ctypes.c_int(0)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = _lib.ada_decode_partial(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens_t), B, Hq, Hkv, D, S, mkl,
+                                 ctypes.c_float(scale), _DTYPE_CODES[k_cache.dtype], int(num_splits), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), ctypes.byref(used),
+                                 ctypes.c_void_p(_stream(k_cache.device)))
+    _check(rc, "ada_decode_partial")
+    return workspace, used.value
+
+
+def decode_combine(workspace: torch.Tensor, num_splits: int, out: torch.Tensor, n_kv_head: int) -> torch.Tensor:
+    """Second half of a decode call: merge ``num_splits`` split-major partials
+    in ``workspace`` into ``out`` [B, Hq, D] (or [B, Hq, 1, D])."""
+    _require(out.is_cuda and out.is_contiguous() and out.dtype in _DTYPE_CODES, "out must be a contiguous 16-bit GPU tensor")
+    _require(workspace.is_cuda and workspace.device == out.device, "workspace must be on the output's device")
+    B, Hq, D = out.shape[0], out.shape[1], out.shape[-1]
+    rc = _lib.ada_decode_combine(_ptr(workspace), workspace.numel() * workspace.element_size(), B, Hq, int(n_kv_head),
+                                 D, int(num_splits), _DTYPE_CODES[out.dtype], _ptr(out),
+                                 ctypes.c_void_p(_stream(out.device)))
+    _check(rc, "ada_decode_combine")
+    return out
+
+
+def decode_attn_gqa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len,
+                    scale: float | None = None, out: torch.Tensor | None = None,
+                    max_kv_len: int | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """out = softmax(scale * q K[:kv_len]^T) V[:kv_len] per batch row, grouped-query
+    heads read in place (query head h uses KV head h // (Hq // Hkv)).
+
+    q: [B, Hq, D] or [B, Hq, 1, D]; caches [B, Hkv, S, D]; kv_len: int32 GPU
+    tensor [B] (then ``max_kv_len`` bounds it, default S) or host ints. Returns
+    ``out`` (allocated like q when not given). Runs on the current stream."""
+    return decode_attn_gqa_ex(q, k_cache, v_cache, kv_len, scale=scale, out=out, max_kv_len=max_kv_len,
+                              num_splits=0, workspace=workspace)
+
+
+__all__ = [
+    "AdaError", "F16", "BF16", "HEAD_DIM", "MAX_SPLITS", "EXPORTS", "LIB_PATH", "load_library",
+    "kv_append", "decode_attn_gqa", "decode_attn_gqa_ex", "decode_partial", "decode_combine", "decode_num_splits", "decode_workspace_bytes",
+    "new_workspace", "workspace_layout", "device_num_cus", "status_string", "last_hip_error",
+    "abi_version",
+]

@@ -1,0 +1,290 @@
+// ada_api.cpp -- the C ABI of libada: host-side validation, the split
+// heuristic, workspace arithmetic and dispatch to the gfx950 kernels.
+//
+// Every argument is checked before the first HIP call, so a rejected call
+// has no effect and the checks run without a GPU. The ABI itself is
+// documented in include/ada.h.
+#include "ada.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "ada_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+// Compute-unit count per HIP device, filled on first use (0 = not yet known).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_num_cus[kMaxDevices];
+
+int hip_fail(hipError_t e) {
+  g_last_hip_error = static_cast<int>(e);
+  return ADA_ERR_HIP;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int current_device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev >= 0 && dev < kMaxDevices) {
+    int cached = g_num_cus[dev].load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *cus = cached;
+      return ADA_OK;
+    }
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (n <= 0) n = 1;
+  if (dev >= 0 && dev < kMaxDevices) g_num_cus[dev].store(n, std::memory_order_relaxed);
+  *cus = n;
+  return ADA_OK;
+}
+
+// Split plan: chunk = slots per split; splits = number of split workgroups
+// per (batch row, KV head) actually launched.
+struct Plan {
+  int splits;
+  int chunk;
+};
+
+// Forced split count: near-equal ranges, no rounding beyond one slot.
+Plan forced_plan(int max_kv_len, int requested) {
+  if (max_kv_len <= 0) return {1, 1};
+  int chunk = static_cast<int>(ceil_div(max_kv_len, requested));
+  if (chunk < 1) chunk = 1;
+  return {static_cast<int>(ceil_div(max_kv_len, chunk)), chunk};
+}
+
+// Heuristic: about two 4-wave workgroups per compute unit, every split at
+// least 128 slots, ranges rounded up to whole 64-slot tiles.
+Plan heuristic_plan(int batch, int n_kv_head, int max_kv_len, int num_cus) {
+  if (batch <= 0 || n_kv_head <= 0 || max_kv_len <= 0 || num_cus <= 0) return {1, max_kv_len > 0 ? max_kv_len : 1};
+  const int64_t units = static_cast<int64_t>(batch) * n_kv_head;
+  const int64_t target_wgs = 2 * static_cast<int64_t>(num_cus);
+  int64_t splits = ceil_div(target_wgs, units);
+  const int64_t by_len = ceil_div(max_kv_len, 128);
+  if (splits > by_len) splits = by_len;
+  if (splits > ADA_MAX_SPLITS) splits = ADA_MAX_SPLITS;
+  if (splits < 1) splits = 1;
+  int64_t chunk = ceil_div(ceil_div(max_kv_len, splits), ada::kTileRows) * ada::kTileRows;
+  return {static_cast<int>(ceil_div(max_kv_len, chunk)), static_cast<int>(chunk)};
+}
+
+}  // namespace
+
+namespace ada {
+
+WorkspaceLayout workspace_layout(int batch, int n_head, int n_kv_head, int head_dim, int splits) {
+  WorkspaceLayout w{};
+  auto round256 = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const size_t rows = static_cast<size_t>(batch) * n_head * splits;
+  (void)n_kv_head;
+  w.ml_offset = 0;
+  w.acc_offset = w.ml_offset + round256(rows * 2 * sizeof(float));
+  w.total = w.acc_offset + round256(rows * static_cast<size_t>(head_dim) * sizeof(float));
+  return w;
+}
+
+}  // namespace ada
+
+extern "C" {
+
+int ada_abi_version(void) { return ADA_ABI_VERSION; }
+
+const char* ada_status_string(int status) {
+  switch (status) {
+    case ADA_OK: return "ok";
+    case ADA_ERR_NULL: return "a required pointer is NULL";
+    case ADA_ERR_SHAPE: return "batch, head count, capacity or max_kv_len out of range";
+    case ADA_ERR_GQA: return "n_head must be a multiple of n_kv_head with group size 1..8";
+    case ADA_ERR_DTYPE: return "dtype must be ADA_F16 or ADA_BF16";
+    case ADA_ERR_HEAD_DIM: return "head_dim must be 128";
+    case ADA_ERR_SCALE: return "scale must be finite";
+    case ADA_ERR_WORKSPACE: return "workspace missing or too small for the split count";
+    case ADA_ERR_SPLITS: return "num_splits out of range";
+    case ADA_ERR_ALIGN: return "device pointers must be 16-byte aligned";
+    case ADA_ERR_HIP: return "HIP runtime error (see ada_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int ada_last_hip_error(void) { return g_last_hip_error; }
+
+int ada_device_num_cus(int device, int* num_cus) {
+  if (!num_cus) return ADA_ERR_NULL;
+  int n = 0;
+  hipError_t e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device);
+  if (e != hipSuccess) return hip_fail(e);
+  *num_cus = n;
+  return ADA_OK;
+}
+
+int ada_decode_num_splits(int batch, int n_kv_head, int max_kv_len, int num_cus) {
+  return heuristic_plan(batch, n_kv_head, max_kv_len, num_cus).splits;
+}
+
+size_t ada_decode_workspace_bytes(int batch, int n_head, int n_kv_head, int head_dim, int num_splits) {
+  if (num_splits < 1 || batch <= 0 || n_head <= 0 || n_kv_head <= 0 || head_dim <= 0) return 0;
+  return ada::workspace_layout(batch, n_head, n_kv_head, head_dim, num_splits).total;
+}
+
+int ada_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  const int32_t* pos, int batch, int n_kv_head, int capacity, int head_dim,
+                  int dtype, void* stream) {
+  if (dtype != ADA_F16 && dtype != ADA_BF16) return ADA_ERR_DTYPE;
+  if (batch < 0 || n_kv_head <= 0 || capacity <= 0) return ADA_ERR_SHAPE;
+  if (head_dim != ada::kHeadDim) return ADA_ERR_HEAD_DIM;
+  if (batch == 0) return ADA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !pos) return ADA_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))
+    return ADA_ERR_ALIGN;
+  hipError_t e = ada::launch_kv_append(k_new, v_new, k_cache, v_cache, pos, batch, n_kv_head,
+                                       capacity, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ADA_OK : hip_fail(e);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the decode entry points; fills the launch description
+// except out/workspace/direct. Returns ADA_OK or the status to report.
+int prepare_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,
+                   int batch, int n_head, int n_kv_head, int head_dim, int capacity,
+                   int max_kv_len, float scale, int dtype, int num_splits, void* stream,
+                   ada::DecodeLaunch* p) {
+  if (dtype != ADA_F16 && dtype != ADA_BF16) return ADA_ERR_DTYPE;
+  if (batch < 0 || n_head <= 0 || n_kv_head <= 0 || capacity <= 0) return ADA_ERR_SHAPE;
+  if (n_head % n_kv_head != 0 || n_head / n_kv_head > ada::kMaxGroup) return ADA_ERR_GQA;
+  if (head_dim != ada::kHeadDim) return ADA_ERR_HEAD_DIM;
+  if (!std::isfinite(scale)) return ADA_ERR_SCALE;
+  if (max_kv_len <= 0) max_kv_len = capacity;
+  if (max_kv_len > capacity) return ADA_ERR_SHAPE;
+  if (num_splits < 0 || num_splits > ADA_MAX_SPLITS) return ADA_ERR_SPLITS;
+  if (batch > 65535 || n_kv_head > 65535) return ADA_ERR_SHAPE;  // grid limits
+  if (batch == 0) return ADA_OK;
+  if (!q || !k_cache || !v_cache || !kv_len) return ADA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return ADA_ERR_ALIGN;
+
+  Plan plan{};
+  if (num_splits > 0) {
+    plan = forced_plan(max_kv_len, num_splits);
+  } else {
+    int cus = 0;
+    int rc = current_device_cus(&cus);
+    if (rc != ADA_OK) return rc;
+    plan = heuristic_plan(batch, n_kv_head, max_kv_len, cus);
+  }
+  *p = ada::DecodeLaunch{};
+  p->q = q;
+  p->k_cache = k_cache;
+  p->v_cache = v_cache;
+  p->kv_len = kv_len;
+  p->batch = batch;
+  p->n_head = n_head;
+  p->n_kv_head = n_kv_head;
+  p->capacity = capacity;
+  p->max_kv_len = max_kv_len;
+  p->splits = plan.splits;
+  p->chunk = plan.chunk;
+  p->scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  p->dtype = dtype;
+  p->stream = static_cast<hipStream_t>(stream);
+  return ADA_OK;
+}
+
+int check_workspace(const void* workspace, size_t workspace_bytes, int batch, int n_head,
+                    int n_kv_head, int splits) {
+  const size_t need = ada::workspace_layout(batch, n_head, n_kv_head, ada::kHeadDim, splits).total;
+  if (!workspace || workspace_bytes < need) return ADA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ADA_ERR_ALIGN;
+  return ADA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ada_decode_attn_gqa_ex(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* kv_len, int batch, int n_head, int n_kv_head,
+                           int head_dim, int capacity, int max_kv_len, float scale, int dtype,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream,
+                           int num_splits) {
+  ada::DecodeLaunch p{};
+  int rc = prepare_decode(q, k_cache, v_cache, kv_len, batch, n_head, n_kv_head, head_dim, capacity,
+                          max_kv_len, scale, dtype, num_splits, stream, &p);
+  if (rc != ADA_OK || batch == 0) return rc;
+  if (!out) return ADA_ERR_NULL;
+  if (!aligned16(out)) return ADA_ERR_ALIGN;
+  p.out = out;
+  p.direct = p.splits == 1;
+  if (!p.direct) {
+    rc = check_workspace(workspace, workspace_bytes, batch, n_head, n_kv_head, p.splits);
+    if (rc != ADA_OK) return rc;
+    p.workspace = workspace;
+  }
+  hipError_t e = ada::launch_partial(p);
+  if (e != hipSuccess) return hip_fail(e);
+  if (p.direct) return ADA_OK;
+  ada::CombineLaunch c{workspace, out, batch, n_head, n_kv_head, p.splits, dtype, p.stream};
+  e = ada::launch_combine(c);
+  return e == hipSuccess ? ADA_OK : hip_fail(e);
+}
+
+int ada_decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* kv_len, int batch, int n_head, int n_kv_head, int head_dim,
+                        int capacity, int max_kv_len, float scale, int dtype, void* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  return ada_decode_attn_gqa_ex(q, k_cache, v_cache, kv_len, batch, n_head, n_kv_head, head_dim,
+                                capacity, max_kv_len, scale, dtype, out, workspace,
+                                workspace_bytes, stream, 0);
+}
+
+int ada_decode_partial(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* kv_len, int batch, int n_head, int n_kv_head, int head_dim,
+                       int capacity, int max_kv_len, float scale, int dtype, int num_splits,
+                       void* workspace, size_t workspace_bytes, int* splits_used, void* stream) {
+  ada::DecodeLaunch p{};
+  int rc = prepare_decode(q, k_cache, v_cache, kv_len, batch, n_head, n_kv_head, head_dim, capacity,
+                          max_kv_len, scale, dtype, num_splits, stream, &p);
+  if (rc != ADA_OK) return rc;
+  if (splits_used) *splits_used = batch == 0 ? 0 : p.splits;
+  if (batch == 0) return ADA_OK;
+  rc = check_workspace(workspace, workspace_bytes, batch, n_head, n_kv_head, p.splits);
+  if (rc != ADA_OK) return rc;
+  p.workspace = workspace;
+  p.direct = false;
+  hipError_t e = ada::launch_partial(p);
+  return e == hipSuccess ? ADA_OK : hip_fail(e);
+}
+
+int ada_decode_combine(const void* workspace, size_t workspace_bytes, int batch, int n_head,
+                       int n_kv_head, int head_dim, int num_splits, int dtype, void* out,
+                       void* stream) {
+  if (dtype != ADA_F16 && dtype != ADA_BF16) return ADA_ERR_DTYPE;
+  if (batch < 0 || n_head <= 0 || n_kv_head <= 0) return ADA_ERR_SHAPE;
+  if (n_head % n_kv_head != 0 || n_head / n_kv_head > ada::kMaxGroup) return ADA_ERR_GQA;
+  if (head_dim != ada::kHeadDim) return ADA_ERR_HEAD_DIM;
+  if (num_splits < 1 || num_splits > ADA_MAX_SPLITS) return ADA_ERR_SPLITS;
+  if (batch > 65535 || n_kv_head > 65535) return ADA_ERR_SHAPE;
+  if (batch == 0) return ADA_OK;
+  if (!out) return ADA_ERR_NULL;
+  if (!aligned16(out)) return ADA_ERR_ALIGN;
+  int rc = check_workspace(workspace, workspace_bytes, batch, n_head, n_kv_head, num_splits);
+  if (rc != ADA_OK) return rc;
+  ada::CombineLaunch c{workspace, out, batch, n_head, n_kv_head, num_splits, dtype,
+                       static_cast<hipStream_t>(stream)};
+  hipError_t e = ada::launch_combine(c);
+  return e == hipSuccess ? ADA_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// ada_internal.h -- launchers shared between the C ABI layer (ada_api.cpp)
+// and the kernels (ada_kernels.hip). Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ada {
+
+constexpr int kHeadDim = 128;
+constexpr int kMaxGroup = 8;
+constexpr int kThreads = 256;    // 4 wavefronts of 64
+constexpr int kTileRows = 64;    // slot granularity the heuristic rounds split ranges to
+constexpr int kMaxSplits = 256;  // equals ADA_MAX_SPLITS
+
+// Workspace layout for `splits` splits, split-major (the partials of one
+// split are contiguous, so partials computed on separate key ranges can be
+// concatenated along the split axis and combined together):
+//   [ml_offset, +ml_bytes)       float2 (running max in log2 units, sum) per
+//                                (split, batch row, query head); m = -inf
+//                                marks an empty split
+//   [acc_offset, +acc_bytes)     float[head_dim] unnormalised accumulator per
+//                                (split, batch row, query head)
+struct WorkspaceLayout {
+  size_t ml_offset;
+  size_t acc_offset;
+  size_t total;
+};
+
+WorkspaceLayout workspace_layout(int batch, int n_head, int n_kv_head, int head_dim, int splits);
+
+struct DecodeLaunch {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* kv_len;
+  void* out;        // written when direct
+  void* workspace;  // partials written when !direct
+  int batch, n_head, n_kv_head, capacity, max_kv_len;
+  int splits, chunk;
+  bool direct;       // one split: write the output, no partials
+  float scale_log2;  // scale * log2(e)
+  int dtype;         // 0 fp16, 1 bf16
+  hipStream_t stream;
+};
+
+struct CombineLaunch {
+  const void* workspace;
+  void* out;
+  int batch, n_head, n_kv_head, splits;
+  int dtype;
+  hipStream_t stream;
+};
+
+hipError_t launch_partial(const DecodeLaunch& p);
+hipError_t launch_combine(const CombineLaunch& p);
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            const int32_t* pos, int batch, int n_kv_head, int capacity,
+                            hipStream_t stream);
+
+}  // namespace ada

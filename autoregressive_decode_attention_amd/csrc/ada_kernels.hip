@@ -1,0 +1,596 @@
+// ada_kernels.hip -- gfx950 kernels of libada: single-token decode attention
+// over the active prefix of a preallocated KV cache, and the in-place append.
+//
+// Pages cited (by title and section):
+//   [DECODE-FASTPATH] Cuda-Compute-OSS issue #343, "one-token decode fast
+//                     path: skip FlashAttention's prefill-tuned tiling for
+//                     q_len=1".
+//   [ACTIVE-PREFIX]   fish-speech issue #1310, "Optimize native AR decoding
+//                     by attending only to the active KV-cache prefix".
+//   [FORWARD-STEP]    VoxCPM issue #395, "MiniCPM4
+//                     MiniCPMAttention.forward_step Attention Performance Fix".
+//
+// The decode step reads every live K and V row once per KV head and does a
+// few flops per byte, so it is bound by HBM bandwidth ([DECODE-FASTPATH],
+// "Current limitation"). The design follows from that:
+//
+//   * Partial kernel: one workgroup (4 wavefronts) per (key-range split, KV
+//     head, batch row). Each K/V row it loads serves all G = n_head /
+//     n_kv_head query heads of the group: KV heads are never expanded
+//     ([ACTIVE-PREFIX] section 1).
+//   * Lane layout: L lanes per key row (8 for G <= 4, 16 above), each lane
+//     holding 8 or 16 head dims in 16-byte chunks, so one 16-byte load per
+//     lane covers 64 / L consecutive rows in contiguous 128- or 256-byte
+//     runs: fully coalesced. Loads run P tiles ahead of the compute through a
+//     register ring.
+//   * q.k in fp32 with the packed 16-bit dot instructions (products of two
+//     16-bit values are exact in fp32), summed over the L lanes of a row with
+//     DPP butterfly adds; scale*log2(e) is applied to the sum.
+//   * Online softmax in base 2 per lane group (running max m, sum l, fp32
+//     accumulator), rescaling only when a running maximum grows; lane groups
+//     are merged with DPP and the 16/32-lane permlane swaps, wavefronts
+//     through LDS.
+//   * With one split the workgroup writes the output directly. With several
+//     splits each workgroup stores its (m, l, acc) partial and a second,
+//     small kernel merges a row's partials in split order (log-sum-exp
+//     weights), so the result does not depend on scheduling. The kernel
+//     boundary publishes the partials once per launch; a per-workgroup
+//     device-scope release (which writes back the L2 of the workgroup's XCD)
+//     measured far slower on this chip once workgroups number in the hundreds.
+//   * Slots at and beyond kv_len[b] are never loaded: the tail may hold
+//     anything ([ACTIVE-PREFIX] section 2; [FORWARD-STEP] section 3).
+//   * fp32 -> fp16/bf16 output conversion rounds to nearest even
+//     ([DECODE-FASTPATH], "Proposed implementation": cast back to the input
+//     type).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ada_internal.h"
+
+namespace ada {
+namespace {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = kThreads / 64;
+constexpr float kNegInf = -__builtin_inff();
+
+struct F16 {
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c,
+                                  false);
+  }
+  static __device__ __forceinline__ void unpack(uint32_t u, float& lo, float& hi) {
+    f16x2 h = __builtin_bit_cast(f16x2, u);
+    lo = static_cast<float>(h.x);
+    hi = static_cast<float>(h.y);
+  }
+  static __device__ __forceinline__ uint16_t round(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  }
+};
+
+struct BF16 {
+  static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+  }
+  static __device__ __forceinline__ void unpack(uint32_t u, float& lo, float& hi) {
+    lo = __uint_as_float(u << 16);
+    hi = __uint_as_float(u & 0xffff0000u);
+  }
+  static __device__ __forceinline__ uint16_t round(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Cross-lane reductions. A "row" of the hardware is 16 lanes; DPP moves data
+// within a row, the permlane swaps exchange rows 16 and 32 lanes apart.
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each 8
+constexpr int kDppRor8 = 0x128;       // lane i <- lane i^8 within each 16
+
+struct Sum {
+  static __device__ __forceinline__ float op(float a, float b) { return a + b; }
+};
+struct Max {
+  static __device__ __forceinline__ float op(float a, float b) { return fmaxf(a, b); }
+};
+
+template <class Op>
+__device__ __forceinline__ float xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return Op::op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+template <class Op>
+__device__ __forceinline__ float xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return Op::op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Reduce over the L consecutive lanes of a lane group (L = 8 or 16).
+template <int L>
+__device__ __forceinline__ float lane_group_sum(float x) {
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  x += dpp<kDppHalfMirror>(x);
+  if constexpr (L == 16) x += dpp<kDppRor8>(x);
+  return x;
+}
+
+// Reduce over the 64 / L lane groups of a wavefront (lanes equal modulo L).
+template <int L, class Op>
+__device__ __forceinline__ float across_groups(float x) {
+  if constexpr (L == 8) x = Op::op(x, dpp<kDppRor8>(x));
+  x = xor16<Op>(x);
+  return xor32<Op>(x);
+}
+
+// Reduce over all 64 lanes.
+template <class Op>
+__device__ __forceinline__ float wave_reduce(float x) {
+  x = Op::op(x, dpp<kDppXor1>(x));
+  x = Op::op(x, dpp<kDppXor2>(x));
+  x = Op::op(x, dpp<kDppHalfMirror>(x));
+  x = Op::op(x, dpp<kDppRor8>(x));
+  x = xor16<Op>(x);
+  return xor32<Op>(x);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reference for exp2(m - ref): the running maximum itself, or 0 while it is
+// still -inf (nothing seen yet), so that an empty state weighs exp2(-inf) = 0.
+__device__ __forceinline__ float finite_ref(float m) { return m == kNegInf ? 0.0f : m; }
+
+__device__ __forceinline__ uint4 load16(const uint16_t* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+template <class E>
+__device__ __forceinline__ void unpack8(const uint4& u, float* f) {
+  E::unpack(u.x, f[0], f[1]);
+  E::unpack(u.y, f[2], f[3]);
+  E::unpack(u.z, f[4], f[5]);
+  E::unpack(u.w, f[6], f[7]);
+}
+
+template <class E>
+__device__ __forceinline__ float dot8(const uint4& k, const uint4& q, float s) {
+  s = E::dot2(k.x, q.x, s);
+  s = E::dot2(k.y, q.y, s);
+  s = E::dot2(k.z, q.z, s);
+  return E::dot2(k.w, q.w, s);
+}
+
+// ---------------------------------------------------------------------------
+// Decode kernel.
+//
+// Template parameters:
+//   G  query heads per KV head (1..8)
+//   L  lanes per key row (8: 16 dims per lane; 16: 8 dims per lane)
+//   T  rows per lane group per tile
+//   P  tiles in flight ahead of the one being computed (register ring of
+//      P + 1 tiles; the ring is unrolled so buffers never move)
+template <class E, int G, int L, int T, int P>
+__global__ __launch_bounds__(kThreads) void partial_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
+    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ kv_len,
+    uint16_t* __restrict__ out, float2* __restrict__ part_ml, float* __restrict__ part_acc, int n_kv_head, int capacity, int max_kv_len, int chunk,
+    int direct, float scale_log2) {
+  constexpr int D = kHeadDim;
+  constexpr int CH = 16 / L;             // 16-byte chunks per lane per row
+  constexpr int DPL = 8 * CH;            // dims per lane
+  constexpr int kRows = 64 / L;          // rows covered by one wave-wide load
+  constexpr int kWaveRows = kRows * T;   // rows per wave per tile
+  constexpr int kTile = kWaveRows * kWaves;
+  constexpr int NB = P + 1;
+
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int n_head = n_kv_head * G;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int grp = lane / L;   // row of this lane within a wave-wide load
+  const int sub = lane % L;   // dims [8*sub, +8) (and [64 + 8*sub, +8) when L == 8)
+
+  int n = kv_len[b];
+  n = n < 0 ? 0 : (n > max_kv_len ? max_kv_len : n);
+  const int nsplit = (n + chunk - 1) / chunk;  // splits holding live slots
+  const size_t out_row0 = (static_cast<size_t>(b) * n_head + static_cast<size_t>(g) * G) * D;
+
+  // Partials are split-major: entry (split, batch row, query head).
+  const size_t head_row0 = static_cast<size_t>(b) * n_head + static_cast<size_t>(g) * G;
+  const size_t part_row0 = static_cast<size_t>(split) * gridDim.z * n_head + head_row0;
+  if (split >= nsplit) {
+    if (direct) {           // empty prefix, output written here: the empty sum, a zero row
+      for (int idx = tid; idx < G * D; idx += kThreads) out[out_row0 + idx] = 0;
+    } else if (tid < G) {   // mark the split empty for the combine
+      part_ml[part_row0 + tid] = make_float2(kNegInf, 0.0f);
+    }
+    return;
+  }
+  const int row_begin = split * chunk;
+  const int row_end = min(row_begin + chunk, n);
+
+  uint4 qv[G][CH];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) qv[i][c] = load16(q + out_row0 + static_cast<size_t>(i) * D + 8 * sub + 64 * c);
+  }
+
+  float m[G], l[G], acc[G][DPL];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    m[i] = kNegInf;
+    l[i] = 0.0f;
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) acc[i][d] = 0.0f;
+  }
+
+  const size_t head_off = (static_cast<size_t>(b) * n_kv_head + g) * static_cast<size_t>(capacity) * D;
+  const uint16_t* kbase = k_cache + head_off + 8 * sub;
+  const uint16_t* vbase = v_cache + head_off + 8 * sub;
+
+  const int wave_first = row_begin + wave * kWaveRows;
+  const int span = row_end - wave_first;
+  const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;  // same for the whole wave
+  const int my_first = wave_first + grp;
+  const int last_row = row_end - 1;
+
+  // Rows past the split's end are loaded from its last live row (always in
+  // bounds and finite) and given zero weight, so no branch guards the loads.
+  uint4 kb[NB][T][CH], vb[NB][T][CH];
+  auto load_tile = [&](int base, uint4 (&kr)[T][CH], uint4 (&vr)[T][CH]) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int r = min(base + t * kRows, last_row);
+      const size_t off = static_cast<size_t>(r) * D;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        kr[t][c] = load16(kbase + off + 64 * c);
+        vr[t][c] = load16(vbase + off + 64 * c);
+      }
+    }
+  };
+
+  auto process = [&](int base, const uint4 (&kr)[T][CH], const uint4 (&vr)[T][CH]) {
+    float x[T][G];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const bool valid = base + t * kRows <= last_row;
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        float s = 0.0f;
+#pragma unroll
+        for (int c = 0; c < CH; ++c) s = dot8<E>(kr[t][c], qv[i][c], s);
+        s = lane_group_sum<L>(s);
+        x[t][i] = valid ? s * scale_log2 : kNegInf;
+      }
+    }
+    // Rescale only when some lane group's running maximum grows.
+    float mt[G];
+    bool grow = false;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      mt[i] = x[0][i];
+#pragma unroll
+      for (int t = 1; t < T; ++t) mt[i] = fmaxf(mt[i], x[t][i]);
+      grow |= mt[i] > m[i];
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const float m_new = fmaxf(m[i], mt[i]);
+        const float alpha = fast_exp2(m[i] - finite_ref(m_new));
+        l[i] *= alpha;
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) acc[i][d] *= alpha;
+        m[i] = m_new;
+      }
+    }
+    float p[T][G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float ref = finite_ref(m[i]);
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        p[t][i] = fast_exp2(x[t][i] - ref);
+        l[i] += p[t][i];
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      float vf[DPL];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) unpack8<E>(vr[t][c], vf + 8 * c);
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+#pragma unroll
+        for (int d = 0; d < DPL; ++d) acc[i][d] = fmaf(p[t][i], vf[d], acc[i][d]);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int pf = 0; pf < P; ++pf) {
+    if (pf < ntiles) load_tile(my_first + pf * kTile, kb[pf], vb[pf]);
+  }
+  for (int t0 = 0; t0 < ntiles; t0 += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int t = t0 + u;
+      if (t < ntiles) {
+        if (t + P < ntiles) load_tile(my_first + (t + P) * kTile, kb[(u + P) % NB], vb[(u + P) % NB]);
+        process(my_first + t * kTile, kb[u], vb[u]);
+      }
+    }
+  }
+
+  // Merge the lane groups of the wavefront (lanes equal modulo L hold the
+  // same dims of different rows): common maximum, then rescaled sums.
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const float mw = across_groups<L, Max>(m[i]);
+    const float sc = fast_exp2(m[i] - finite_ref(mw));
+    l[i] = across_groups<L, Sum>(l[i] * sc);
+#pragma unroll
+    for (int d = 0; d < DPL; ++d) acc[i][d] = across_groups<L, Sum>(acc[i][d] * sc);
+    m[i] = mw;
+  }
+
+  // Merge the 4 wavefronts through LDS.
+  __shared__ float s_acc[kWaves][G][D];
+  __shared__ float2 s_ml[kWaves][G];
+  if (lane < L) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) s_acc[wave][i][8 * sub + 64 * c + d] = acc[i][8 * c + d];
+      }
+      if (lane == 0) s_ml[wave][i] = make_float2(m[i], l[i]);
+    }
+  }
+  __syncthreads();
+
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int i = idx / D;
+    const int d = idx % D;
+    float mw = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mw = fmaxf(mw, s_ml[w][i].x);
+    const float ref = finite_ref(mw);
+    float lsum = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = fast_exp2(s_ml[w][i].x - ref);
+      lsum += s_ml[w][i].y * wt;
+      o += s_acc[w][i][d] * wt;
+    }
+    if (direct) {
+      out[out_row0 + idx] = E::round(o / lsum);
+    } else {
+      const size_t pr = part_row0 + i;
+      part_acc[pr * D + d] = o;
+      if (d == 0) part_ml[pr] = make_float2(mw, lsum);
+    }
+  }
+}
+
+// Combine kernel: one workgroup per (KV head, batch row) merges the
+// num_splits partials of the row's G heads, in split order, with log-sum-exp
+// weights:
+//   M = max_s m_s, w_s = exp2(m_s - M) / sum_s exp2(m_s - M) l_s,
+//   out = sum_s w_s acc_s,
+// then rounds to the output type. Empty splits carry m = -inf and weigh 0
+// (their accumulators are never used); a row whose splits are all empty
+// (kv_len 0) gets zeros. kv_len is not read: the marks say everything.
+//
+// Column = 4 consecutive dims of one head; R threads share a column and take
+// every R-th split. The first batch of accumulator loads is issued together
+// with the (m, l) loads, so the workgroup waits for memory once.
+template <class E, int G>
+__global__ __launch_bounds__(kThreads) void combine_kernel(
+    uint16_t* __restrict__ out, const float2* __restrict__ part_ml,
+    const float* __restrict__ part_acc, int n_kv_head, int num_splits) {
+  constexpr int D = kHeadDim;
+  constexpr int kCols = G * (D / 4);
+  constexpr int R = kThreads / kCols;
+  constexpr int kBatch = 8;
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
+  const int n_head = n_kv_head * G;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int ns = num_splits;
+
+  __shared__ float2 s_pml[G][kMaxSplits];
+  __shared__ float4 s_red[R > 1 ? R : 1][kCols];
+  const size_t out_row0 = (static_cast<size_t>(b) * n_head + static_cast<size_t>(g) * G) * D;
+  const size_t head_row0 = static_cast<size_t>(b) * n_head + static_cast<size_t>(g) * G;
+  const size_t split_stride = static_cast<size_t>(gridDim.y) * n_head;  // split-major partials
+  const int col = tid % kCols;
+  const int r = tid / kCols;
+  const bool active = r < R;
+  const int ci = col / (D / 4);
+  const int cd = (col % (D / 4)) * 4;
+  const float4* acc4 = reinterpret_cast<const float4*>(part_acc);
+  const size_t col_row0 = head_row0 + ci;
+
+  float4 av[kBatch];
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int s = r + k * R;
+    if (active && s < ns) av[k] = acc4[((col_row0 + s * split_stride) * D + cd) / 4];
+  }
+  for (int e = tid; e < G * ns; e += kThreads) {
+    const int i = e / ns;
+    const int s = e % ns;
+    s_pml[i][s] = part_ml[head_row0 + i + s * split_stride];
+  }
+  __syncthreads();
+  // Per head (one wave per head): maximum and normaliser over the splits,
+  // then each split's weight exp2(m_s - M) / L, stored in place of its m.
+  for (int i = wave; i < G; i += kWaves) {
+    float mx = kNegInf;
+    for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, s_pml[i][s].x);
+    mx = wave_reduce<Max>(mx);
+    const float ref = finite_ref(mx);
+    float ls = 0.0f;
+    for (int s = lane; s < ns; s += 64) ls += s_pml[i][s].y * fast_exp2(s_pml[i][s].x - ref);
+    ls = wave_reduce<Sum>(ls);
+    const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
+    for (int s = lane; s < ns; s += 64) s_pml[i][s].x = fast_exp2(s_pml[i][s].x - ref) * inv;
+  }
+  __syncthreads();
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add = [&](float w, const float4& a) {
+    if (w > 0.0f) {  // empty splits (w == 0) hold stale accumulators: skip, never multiply
+      o.x = fmaf(w, a.x, o.x);
+      o.y = fmaf(w, a.y, o.y);
+      o.z = fmaf(w, a.z, o.z);
+      o.w = fmaf(w, a.w, o.w);
+    }
+  };
+  if (active) {
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int s = r + k * R;
+      if (s < ns) add(s_pml[ci][s].x, av[k]);
+    }
+    for (int s = r + kBatch * R; s < ns; s += R) {
+      const float w = s_pml[ci][s].x;
+      if (w > 0.0f) add(w, acc4[((col_row0 + s * split_stride) * D + cd) / 4]);
+    }
+    if (R > 1) s_red[r][col] = o;
+  }
+  if (R > 1) {
+    __syncthreads();
+    if (r == 0) {
+      for (int k = 1; k < R; ++k) {
+        const float4 a = s_red[k][col];
+        o.x += a.x;
+        o.y += a.y;
+        o.z += a.z;
+        o.w += a.w;
+      }
+    }
+  }
+  if (r == 0) {
+    const uint32_t lo = static_cast<uint32_t>(E::round(o.x)) | (static_cast<uint32_t>(E::round(o.y)) << 16);
+    const uint32_t hi = static_cast<uint32_t>(E::round(o.z)) | (static_cast<uint32_t>(E::round(o.w)) << 16);
+    *reinterpret_cast<uint2*>(out + out_row0 + static_cast<size_t>(ci) * D + cd) = make_uint2(lo, hi);
+  }
+}
+
+// In-place append: row pos[b] of every KV head of batch row b, K and V, as
+// 16 sixteen-byte chunks per 128-element row ([FORWARD-STEP] section 4).
+__global__ __launch_bounds__(256) void kv_append_kernel(const uint4* __restrict__ k_new,
+                                                        const uint4* __restrict__ v_new,
+                                                        uint4* __restrict__ k_cache,
+                                                        uint4* __restrict__ v_cache,
+                                                        const int32_t* __restrict__ pos,
+                                                        int n_kv_head, int capacity, int rows) {
+  constexpr int kChunks = kHeadDim * 2 / 16;  // 16-byte chunks per row
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * kChunks) return;
+  const int row = idx / kChunks;  // b * n_kv_head + h
+  const int c = idx % kChunks;
+  const int b = row / n_kv_head;
+  const int p = pos[b];
+  if (p < 0 || p >= capacity) return;
+  const size_t dst = (static_cast<size_t>(row) * capacity + p) * kChunks + c;
+  k_cache[dst] = k_new[static_cast<size_t>(row) * kChunks + c];
+  v_cache[dst] = v_new[static_cast<size_t>(row) * kChunks + c];
+}
+
+// Per group size: lanes per row L, rows per lane group per tile T, tiles in
+// flight P. Every choice gives 64-row workgroup tiles, the granularity the
+// split heuristic rounds to.
+template <int G> struct TileConfig;
+template <> struct TileConfig<1> { static constexpr int L = 8, T = 2, P = 3; };
+template <> struct TileConfig<2> { static constexpr int L = 8, T = 2, P = 3; };
+template <> struct TileConfig<3> { static constexpr int L = 8, T = 2, P = 2; };
+template <> struct TileConfig<4> { static constexpr int L = 8, T = 2, P = 2; };
+template <> struct TileConfig<5> { static constexpr int L = 16, T = 4, P = 2; };
+template <> struct TileConfig<6> { static constexpr int L = 16, T = 4, P = 2; };
+template <> struct TileConfig<7> { static constexpr int L = 16, T = 4, P = 2; };
+template <> struct TileConfig<8> { static constexpr int L = 16, T = 4, P = 2; };
+
+template <class E, int G>
+hipError_t launch_partial_g(const DecodeLaunch& p) {
+  using C = TileConfig<G>;
+  static_assert(kWaves * (64 / C::L) * C::T == kTileRows, "workgroup tile must be kTileRows rows");
+  float2* part_ml = nullptr;
+  float* part_acc = nullptr;
+  if (!p.direct) {
+    const WorkspaceLayout w = workspace_layout(p.batch, p.n_head, p.n_kv_head, kHeadDim, p.splits);
+    char* base = static_cast<char*>(p.workspace);
+    part_ml = reinterpret_cast<float2*>(base + w.ml_offset);
+    part_acc = reinterpret_cast<float*>(base + w.acc_offset);
+  }
+  hipLaunchKernelGGL((partial_kernel<E, G, C::L, C::T, C::P>), dim3(p.splits, p.n_kv_head, p.batch),
+                     dim3(kThreads), 0, p.stream, static_cast<const uint16_t*>(p.q),
+                     static_cast<const uint16_t*>(p.k_cache), static_cast<const uint16_t*>(p.v_cache),
+                     p.kv_len, static_cast<uint16_t*>(p.out), part_ml, part_acc, p.n_kv_head,
+                     p.capacity, p.max_kv_len, p.chunk, p.direct ? 1 : 0, p.scale_log2);
+  return hipGetLastError();
+}
+
+template <class E, int G>
+hipError_t launch_combine_g(const CombineLaunch& p) {
+  const WorkspaceLayout w = workspace_layout(p.batch, p.n_head, p.n_kv_head, kHeadDim, p.splits);
+  const char* base = static_cast<const char*>(p.workspace);
+  hipLaunchKernelGGL((combine_kernel<E, G>), dim3(p.n_kv_head, p.batch), dim3(kThreads), 0, p.stream,
+                     static_cast<uint16_t*>(p.out), reinterpret_cast<const float2*>(base + w.ml_offset),
+                     reinterpret_cast<const float*>(base + w.acc_offset), p.n_kv_head, p.splits);
+  return hipGetLastError();
+}
+
+#define ADA_DISPATCH_GROUP(FN, P)                                   \
+  switch ((P).n_head / (P).n_kv_head) {                             \
+    case 1: return (P).dtype == 1 ? FN<BF16, 1>(P) : FN<F16, 1>(P); \
+    case 2: return (P).dtype == 1 ? FN<BF16, 2>(P) : FN<F16, 2>(P); \
+    case 3: return (P).dtype == 1 ? FN<BF16, 3>(P) : FN<F16, 3>(P); \
+    case 4: return (P).dtype == 1 ? FN<BF16, 4>(P) : FN<F16, 4>(P); \
+    case 5: return (P).dtype == 1 ? FN<BF16, 5>(P) : FN<F16, 5>(P); \
+    case 6: return (P).dtype == 1 ? FN<BF16, 6>(P) : FN<F16, 6>(P); \
+    case 7: return (P).dtype == 1 ? FN<BF16, 7>(P) : FN<F16, 7>(P); \
+    case 8: return (P).dtype == 1 ? FN<BF16, 8>(P) : FN<F16, 8>(P); \
+    default: return hipErrorInvalidValue;                           \
+  }
+
+}  // namespace
+
+hipError_t launch_partial(const DecodeLaunch& p) { ADA_DISPATCH_GROUP(launch_partial_g, p) }
+
+hipError_t launch_combine(const CombineLaunch& p) { ADA_DISPATCH_GROUP(launch_combine_g, p) }
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                            const int32_t* pos, int batch, int n_kv_head, int capacity,
+                            hipStream_t stream) {
+  const int rows = batch * n_kv_head;
+  const int total = rows * (kHeadDim * 2 / 16);
+  const int blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(kv_append_kernel, dim3(blocks), dim3(256), 0, stream,
+                     static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new),
+                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), pos, n_kv_head,
+                     capacity, rows);
+  return hipGetLastError();
+}
+
+}  // namespace ada

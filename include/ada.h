@@ -1,0 +1,213 @@
+/*
+ * ada.h -- C ABI of the single-token decode-attention library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The library does one job: the decode step of grouped-query attention for
+ * one new token per sequence,
+ *
+ *     out[b, h, :] = softmax_j( scale * q[b, h, :] . K[b, g, j, :] ) V[b, g, j, :]
+ *     over the active prefix j < kv_len[b] only, with g = h / (n_head / n_kv_head),
+ *
+ * plus the in-place cache append that precedes it. The cache stays
+ * preallocated at its full capacity; only the live prefix is read, in place,
+ * and KV heads are never expanded to the query-head count.
+ *
+ * Pages cited (by title and section):
+ *   [DECODE-FASTPATH] Cuda-Compute-OSS issue #343, "one-token decode fast
+ *                     path: skip FlashAttention's prefill-tuned tiling for
+ *                     q_len=1".
+ *   [ACTIVE-PREFIX]   fish-speech issue #1310, "Optimize native AR decoding
+ *                     by attending only to the active KV-cache prefix".
+ *   [FORWARD-STEP]    VoxCPM issue #395, "MiniCPM4
+ *                     MiniCPMAttention.forward_step Attention Performance
+ *                     Fix".
+ *
+ * Conventions for every entry point:
+ *   - All tensors are dense and row-major (last index fastest); element types
+ *     are IEEE binary16 (ADA_F16) or bfloat16 (ADA_BF16), one type per call.
+ *   - Pointers named as device pointers must point to device memory of the
+ *     current HIP device and be 16-byte aligned. The caller owns every buffer;
+ *     the library allocates no device memory, keeps no per-call state,
+ *     never synchronises, and only enqueues work on `stream` (a hipStream_t;
+ *     NULL is the default stream).
+ *   - Arguments are validated on the host before any HIP call, so a rejected
+ *     call has no effect and needs no GPU. Return value: ADA_OK or a negative
+ *     ada_status. HIP launch failures return ADA_ERR_HIP; the HIP error code
+ *     is then available from ada_last_hip_error() on the calling thread.
+ *   - A call with batch == 0 is a valid no-op (pointers may then be NULL).
+ *   - Only head_dim == 128 is supported (every page uses it).
+ */
+#ifndef ADA_H
+#define ADA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ADA_ABI_VERSION 1
+
+/* Element type of q, caches, new rows and output. */
+typedef enum ada_dtype { ADA_F16 = 0, ADA_BF16 = 1 } ada_dtype;
+
+typedef enum ada_status {
+  ADA_OK = 0,
+  ADA_ERR_NULL = -1,      /* a required pointer is NULL                      */
+  ADA_ERR_SHAPE = -2,     /* batch/heads/capacity/max_kv_len out of range     */
+  ADA_ERR_GQA = -3,       /* n_head not a multiple of n_kv_head, or the group
+                             size n_head / n_kv_head is not 1..8             */
+  ADA_ERR_DTYPE = -4,     /* dtype is not ADA_F16 or ADA_BF16                 */
+  ADA_ERR_HEAD_DIM = -5,  /* head_dim != 128                                  */
+  ADA_ERR_SCALE = -6,     /* scale is not finite                              */
+  ADA_ERR_WORKSPACE = -7, /* workspace NULL or smaller than required          */
+  ADA_ERR_SPLITS = -8,    /* num_splits outside [0, ADA_MAX_SPLITS]           */
+  ADA_ERR_ALIGN = -9,     /* a device pointer is not 16-byte aligned          */
+  ADA_ERR_HIP = -10       /* a HIP runtime call failed                        */
+} ada_status;
+
+/* Upper bound on the number of key-range splits of one decode call. */
+#define ADA_MAX_SPLITS 256
+
+/* Library ABI version (ADA_ABI_VERSION of the build). */
+int ada_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* ada_status_string(int status);
+
+/* hipError_t of the last call on this thread that returned ADA_ERR_HIP. */
+int ada_last_hip_error(void);
+
+/* Number of compute units of HIP device `device`, written to *num_cus.
+ * Returns ADA_ERR_NULL, ADA_ERR_HIP or ADA_OK. */
+int ada_device_num_cus(int device, int* num_cus);
+
+/*
+ * In-place KV-cache append ([FORWARD-STEP] section 4: the new key and value
+ * rows are written at slot position_id of the preallocated cache;
+ * [ACTIVE-PREFIX] section 2: allocation and in-place update are unchanged).
+ *
+ *   k_new, v_new  device, [batch, n_kv_head, head_dim]  (the memory order of
+ *                 the [batch, n_kv_head, 1, head_dim] projection view)
+ *   k_cache,      device, [batch, n_kv_head, capacity, head_dim], updated in
+ *   v_cache       place: row pos[b] of every KV head of batch row b.
+ *   pos           device int32 [batch]. A row with pos[b] outside
+ *                 [0, capacity) is skipped (nothing written), on the device.
+ *
+ * Values are copied bit for bit. k_new/v_new must not overlap the caches.
+ */
+int ada_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                  const int32_t* pos, int batch, int n_kv_head, int capacity,
+                  int head_dim, int dtype, void* stream);
+
+/*
+ * Split heuristic: number of key-range splits for a decode call over
+ * batch * n_kv_head (batch row, KV head) units whose live prefixes are at
+ * most max_kv_len slots, on a device with num_cus compute units. It aims at
+ * two 4-wave workgroups per compute unit without splitting prefixes below
+ * 128 slots, and returns the split count after rounding the per-split slot
+ * range up to a multiple of 64. Pure host arithmetic; returns >= 1 (1 for
+ * non-positive inputs).
+ */
+int ada_decode_num_splits(int batch, int n_kv_head, int max_kv_len, int num_cus);
+
+/*
+ * Bytes of device workspace that holds num_splits (>= 1) per-split partial
+ * results: a running maximum and sum (2 floats) and an unnormalised
+ * accumulator (head_dim floats) per (split, batch row, query head), stored
+ * split-major, each array rounded up to 256 bytes. Returns 0 for
+ * num_splits < 1 or non-positive sizes. ada_decode_attn_gqa needs this much
+ * only when it uses 2 or more splits. n_kv_head is accepted for symmetry
+ * with the decode calls. Pure host arithmetic.
+ */
+size_t ada_decode_workspace_bytes(int batch, int n_head, int n_kv_head, int head_dim,
+                                  int num_splits);
+
+/*
+ * Single-token decode attention with grouped-query heads, over the active
+ * prefix of a preallocated cache, read in place.
+ *
+ * Definition ([DECODE-FASTPATH] "Proposed implementation": softmax of the
+ * scaled q.K row times V, softmax accumulated in fp32, output cast back to
+ * the input type; [ACTIVE-PREFIX] section 2 and [FORWARD-STEP] sections 3-4:
+ * attend over slots [0, kv_len) only, kv_len = position_id + 1 after the
+ * append; [ACTIVE-PREFIX] section 1: query head h reads KV head
+ * h / (n_head / n_kv_head), the repeat_interleave order).
+ *
+ *   q          device, [batch, n_head, head_dim]  (the [B, H, 1, D] query)
+ *   k_cache,   device, [batch, n_kv_head, capacity, head_dim]; only slots
+ *   v_cache    j < n_b are read, n_b = min(max(kv_len[b], 0), max_kv_len).
+ *              Slots at and beyond n_b may hold anything (NaN included).
+ *   kv_len     device int32 [batch], live prefix length per batch row.
+ *   max_kv_len host upper bound on kv_len[b], sizes the launch; <= 0 means
+ *              capacity; > capacity is ADA_ERR_SHAPE. Device values above it
+ *              are clamped to it.
+ *   scale      finite; the pages use 1/sqrt(head_dim). 0 gives equal weights.
+ *   out        device, [batch, n_head, head_dim] (= [B, H*D] as the output
+ *              projection consumes it, [FORWARD-STEP] section 4); must not
+ *              overlap the inputs. Rounded to the element type
+ *              round-to-nearest-even. A row with n_b == 0 is all zeros.
+ *   workspace  device scratch, at least ada_decode_workspace_bytes(...)
+ *              bytes for the split count the call uses (ada_decode_num_splits
+ *              on the current device); may be NULL when that count is 1. Its
+ *              contents need no preparation. Calls that share a workspace
+ *              must be ordered (same stream, or synchronised).
+ *
+ * With one split a single kernel writes the output; with more, a partial
+ * kernel writes per-split results to the workspace and a combine kernel
+ * merges them (log-sum-exp weights, split order). Scores, softmax
+ * statistics and accumulators are fp32. The result is bitwise deterministic
+ * for a given split count.
+ */
+int ada_decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* kv_len, int batch, int n_head, int n_kv_head,
+                        int head_dim, int capacity, int max_kv_len, float scale, int dtype,
+                        void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * As ada_decode_attn_gqa, with the split count forced: num_splits == 0 uses
+ * the heuristic; 1..ADA_MAX_SPLITS splits the key range into that many
+ * near-equal ranges (fewer when max_kv_len is smaller). For tests and tuning.
+ */
+int ada_decode_attn_gqa_ex(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* kv_len, int batch, int n_head, int n_kv_head,
+                           int head_dim, int capacity, int max_kv_len, float scale, int dtype,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream,
+                           int num_splits);
+
+/*
+ * The two halves of a decode call, for callers that merge partial results
+ * themselves -- e.g. key ranges held by different devices, whose partials are
+ * concatenated along the split axis and combined once.
+ *
+ * ada_decode_partial: arguments as ada_decode_attn_gqa_ex without `out`;
+ * always writes partials (never the output) for every split, the split count
+ * it used going to *splits_used (may be NULL). Split s covers slots
+ * [s*c, min((s+1)*c, n_b)) with c = ceil(max_kv_len / splits); its entry
+ * holds m = max of scale*log2(e)*q.k over that range, l = sum of
+ * exp2(score - m), acc = sum of exp2(score - m) * v (fp32, unnormalised); an
+ * empty range holds m = -inf, l = 0 and an accumulator that must not be
+ * read. This is the online (running max and sum) softmax of
+ * [DECODE-FASTPATH], "Current limitation", applied per key range.
+ *
+ * ada_decode_combine: merges num_splits partials per (batch row, query head)
+ * in split order: M = max m_s, out = sum exp2(m_s - M) acc_s /
+ * sum exp2(m_s - M) l_s, rounded to `dtype` round-to-nearest-even; all-empty
+ * rows give zeros. `workspace` holds num_splits partials laid out as
+ * ada_decode_partial writes them (split-major).
+ */
+int ada_decode_partial(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* kv_len, int batch, int n_head, int n_kv_head, int head_dim,
+                       int capacity, int max_kv_len, float scale, int dtype, int num_splits,
+                       void* workspace, size_t workspace_bytes, int* splits_used, void* stream);
+
+int ada_decode_combine(const void* workspace, size_t workspace_bytes, int batch, int n_head,
+                       int n_kv_head, int head_dim, int num_splits, int dtype, void* out,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ADA_H */

@@ -1,0 +1,184 @@
+"""Host side of the C ABI, on the CPU: the library loads, exports every
+function ``include/ada.h`` declares, and rejects every invalid argument
+before any HIP call (no GPU is touched by these tests)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "ada.h"
+
+
+@pytest.fixture(scope="module")
+def ada():
+    lib_path = ROOT / "autoregressive_decode_attention_amd" / "libada.so"
+    if not lib_path.exists():  # CPU container: build it (hipcc cross-compiles gfx950)
+        import importlib.util
+
+        spec = importlib.util.spec_from_file_location("ada_build", lib_path.parent / "build.py")
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
+    import autoregressive_decode_attention_amd as m
+
+    return m
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ada_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("ada_kv_append", "ada_decode_attn_gqa", "ada_decode_attn_gqa_ex",
+                     "ada_decode_num_splits", "ada_decode_workspace_bytes"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(ada):
+    lib = ctypes.CDLL(str(ada.LIB_PATH))
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, f"not exported: {missing}"
+    assert sorted(ada.EXPORTS) == declared_functions()
+
+
+def test_abi_version_and_status_strings(ada):
+    assert ada.abi_version() == 1
+    for code in range(-10, 1):
+        assert ada.status_string(code) and ada.status_string(code) != "unknown status"
+    assert ada.status_string(-99) == "unknown status"
+
+
+# Fake, 16-byte aligned, never dereferenced device addresses: every call below
+# must be rejected by host validation before any HIP call.
+P = ctypes.c_void_p(0x10000)
+P2 = ctypes.c_void_p(0x20000)
+P3 = ctypes.c_void_p(0x30000)
+P4 = ctypes.c_void_p(0x40000)
+P5 = ctypes.c_void_p(0x50000)
+MIS = ctypes.c_void_p(0x10008)
+NUL = ctypes.c_void_p(0)
+
+
+def decode(ada, q=P, k=P2, v=P3, lens=P4, B=1, Hq=32, Hkv=8, D=128, S=2048, mkl=400, scale=0.088,
+           dtype=0, out=P5, ws=NUL, ws_bytes=0, splits=1):
+    return ada._lib.ada_decode_attn_gqa_ex(q, k, v, lens, B, Hq, Hkv, D, S, mkl, ctypes.c_float(scale), dtype,
+                                           out, ws, ws_bytes, NUL, splits)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(dtype=2), -4),
+    (dict(dtype=-1), -4),
+    (dict(q=NUL), -1),
+    (dict(k=NUL), -1),
+    (dict(v=NUL), -1),
+    (dict(lens=NUL), -1),
+    (dict(out=NUL), -1),
+    (dict(B=-1), -2),
+    (dict(Hq=0), -2),
+    (dict(Hkv=0), -2),
+    (dict(S=0), -2),
+    (dict(Hq=30, Hkv=8), -3),
+    (dict(Hq=72, Hkv=8), -3),
+    (dict(D=64), -5),
+    (dict(D=256), -5),
+    (dict(scale=float("inf")), -6),
+    (dict(scale=float("nan")), -6),
+    (dict(mkl=2049), -2),
+    (dict(splits=-1), -8),
+    (dict(splits=257), -8),
+    (dict(q=MIS), -9),
+    (dict(k=MIS), -9),
+    (dict(out=MIS), -9),
+    (dict(splits=2), -7),
+    (dict(splits=2, ws=P, ws_bytes=100), -7),
+    (dict(B=0, q=NUL, k=NUL, v=NUL, lens=NUL, out=NUL), 0),
+])
+def test_decode_validation(ada, kwargs, status):
+    assert decode(ada, **kwargs) == status
+
+
+def test_workspace_too_small_by_one_byte(ada):
+    need = ada.decode_workspace_bytes(1, 32, 8, 128, 3)
+    assert decode(ada, splits=3, ws=P, ws_bytes=need - 1) == -7
+    mis = decode(ada, splits=3, ws=MIS, ws_bytes=need)
+    assert mis == -9
+
+
+def test_append_validation(ada):
+    f = ada._lib.ada_kv_append
+    assert f(P, P2, P3, P4, P5, 1, 8, 16, 128, 5, NUL) == -4
+    assert f(NUL, P2, P3, P4, P5, 1, 8, 16, 128, 0, NUL) == -1
+    assert f(P, P2, P3, P4, NUL, 1, 8, 16, 128, 0, NUL) == -1
+    assert f(P, P2, P3, P4, P5, -1, 8, 16, 128, 0, NUL) == -2
+    assert f(P, P2, P3, P4, P5, 1, 0, 16, 128, 0, NUL) == -2
+    assert f(P, P2, P3, P4, P5, 1, 8, 0, 128, 0, NUL) == -2
+    assert f(P, P2, P3, P4, P5, 1, 8, 16, 64, 0, NUL) == -5
+    assert f(MIS, P2, P3, P4, P5, 1, 8, 16, 128, 0, NUL) == -9
+    assert f(NUL, NUL, NUL, NUL, NUL, 0, 8, 16, 128, 0, NUL) == 0
+
+
+def test_partial_and_combine_validation(ada):
+    part = ada._lib.ada_decode_partial
+    comb = ada._lib.ada_decode_combine
+    used = ctypes.c_int(-1)
+    args = lambda **kw: [kw.get("q", P), P2, P3, kw.get("lens", P4), kw.get("B", 1), 32, 8, kw.get("D", 128), 2048,
+                         400, ctypes.c_float(kw.get("scale", 0.08)), kw.get("dtype", 0), kw.get("splits", 4),
+                         kw.get("ws", NUL), kw.get("ws_bytes", 0), ctypes.byref(used), NUL]
+    assert part(*args(dtype=3)) == -4
+    assert part(*args(q=NUL)) == -1
+    assert part(*args(lens=NUL)) == -1
+    assert part(*args(D=96)) == -5
+    assert part(*args(scale=float("-inf"))) == -6
+    assert part(*args(splits=300)) == -8
+    assert part(*args()) == -7                        # workspace required even for the partials
+    assert part(*args(ws=P, ws_bytes=10)) == -7
+    assert part(*args(B=0, q=NUL, lens=NUL)) == 0 and used.value == 0
+    need = ada.decode_workspace_bytes(1, 32, 8, 128, 4)
+    assert comb(P, need, 1, 32, 8, 128, 0, 0, P5, NUL) == -8
+    assert comb(P, need, 1, 32, 8, 128, 257, 0, P5, NUL) == -8
+    assert comb(P, need - 1, 1, 32, 8, 128, 4, 0, P5, NUL) == -7
+    assert comb(NUL, need, 1, 32, 8, 128, 4, 0, P5, NUL) == -7
+    assert comb(P, need, 1, 32, 8, 128, 4, 0, NUL, NUL) == -1
+    assert comb(P, need, 1, 32, 8, 128, 4, 0, MIS, NUL) == -9
+    assert comb(P, need, 1, 30, 8, 128, 4, 0, P5, NUL) == -3
+    assert comb(P, need, 1, 32, 8, 64, 4, 0, P5, NUL) == -5
+    assert comb(P, need, 1, 32, 8, 128, 4, 7, P5, NUL) == -4
+    assert comb(NUL, 0, 0, 32, 8, 128, 4, 0, NUL, NUL) == 0
+
+
+def test_workspace_bytes_arithmetic(ada):
+    r256 = lambda x: (x + 255) // 256 * 256
+    for B, Hq, Hkv, splits in ((1, 32, 8, 4), (8, 32, 8, 8), (4, 32, 8, 33), (1, 16, 16, 32), (3, 6, 3, 7)):
+        rows = B * Hq * splits
+        want = r256(rows * 8) + r256(rows * 128 * 4)
+        assert ada.decode_workspace_bytes(B, Hq, Hkv, 128, splits) == want
+    assert ada.decode_workspace_bytes(8, 32, 8, 128, 1) == r256(8 * 32 * 8) + r256(8 * 32 * 512)
+    assert ada.decode_workspace_bytes(8, 32, 8, 128, 0) == 0
+    assert ada.decode_workspace_bytes(0, 32, 8, 128, 4) == 0
+
+
+def test_split_heuristic_properties(ada):
+    # worked examples on a 256-CU device
+    assert ada.decode_num_splits(8, 8, 32768, 256) == 8      # long context: 64 units x 8 = 512 workgroups
+    assert ada.decode_num_splits(1, 16, 4096, 256) == 32     # MHA kv 4096: 128-slot splits
+    assert ada.decode_num_splits(1, 8, 400, 256) == 4        # tiny
+    for B in (1, 2, 4, 8, 16, 64):
+        for Hkv in (1, 8, 16):
+            for n in (1, 63, 64, 65, 400, 1258, 4096, 8191, 32768, 131072):
+                s = ada.decode_num_splits(B, Hkv, n, 256)
+                assert 1 <= s <= 256
+                # every split holds at least one live slot and covers the range
+                chunk = -(-n // s)
+                assert -(-n // chunk) == s or s == 1
+                assert s <= max(1, -(-n // 64))
+                # never many more workgroups than two per CU once the batch fills the GPU
+                if B * Hkv >= 512:
+                    assert s == 1
+    assert ada.decode_num_splits(0, 8, 100, 256) == 1
+    assert ada.decode_num_splits(1, 8, 0, 256) == 1
+    assert ada.decode_num_splits(1, 8, 100, 0) == 1
