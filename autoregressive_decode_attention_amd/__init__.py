@@ -200,6 +200,26 @@ def kv_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v
            "ada_kv_append")
 
 
+def _lengths(kv_len, max_kv_len, batch: int, capacity: int, device):
+    """(device lengths or None, max_kv_len) for the C call. A host int, or host
+    ints all equal, become the lockstep form (NULL lengths, max_kv_len = that
+    value, clamped to [0, capacity]); ``None`` means every row holds
+    ``max_kv_len`` slots; a device tensor is passed as is (``max_kv_len``
+    defaults to the capacity); other host lists are copied to the device."""
+    if isinstance(kv_len, torch.Tensor):
+        return _as_int32(kv_len, batch, device), (capacity if max_kv_len is None else int(max_kv_len))
+    if kv_len is None:
+        _require(max_kv_len is not None, "kv_len=None needs max_kv_len")
+        return None, int(max_kv_len)
+    host = [int(v) for v in (kv_len if hasattr(kv_len, "__len__") else [kv_len] * batch)]
+    _require(len(host) == batch, "need one kv_len per batch row")
+    if host and all(v == host[0] for v in host) and max_kv_len is None and host[0] > 0:
+        # (an all-empty batch keeps the device form: max_kv_len <= 0 means "capacity")
+        return None, min(capacity, host[0])
+    mkl = max(1, min(capacity, max(host) if host else 1)) if max_kv_len is None else int(max_kv_len)
+    return _as_int32(host, batch, device), mkl
+
+
 def _as_int32(x, batch: int, device) -> torch.Tensor:
     if isinstance(x, torch.Tensor):
         _require(x.dtype == torch.int32 and x.is_cuda and x.is_contiguous() and x.numel() == batch,
@@ -229,13 +249,7 @@ def decode_attn_gqa_ex(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
         out = torch.empty_like(q)
     _require(out.shape == q.shape and out.dtype == q.dtype and out.device == q.device and out.is_contiguous(),
              "out must be a contiguous tensor like q")
-    if isinstance(kv_len, torch.Tensor):
-        lens_t = _as_int32(kv_len, B, k_cache.device)
-        mkl = S if max_kv_len is None else int(max_kv_len)
-    else:
-        host = [int(v) for v in (kv_len if hasattr(kv_len, "__len__") else [kv_len] * B)]
-        lens_t = _as_int32(host, B, k_cache.device)
-        mkl = max(1, min(S, max(host) if host else 1)) if max_kv_len is None else int(max_kv_len)
+    lens_t, mkl = _lengths(kv_len, max_kv_len, B, S, k_cache.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     plan_len = S if mkl <= 0 else min(mkl, S)  # the library reads max_kv_len <= 0 as the capacity
     if num_splits > 0:
@@ -284,9 +298,7 @@ def decode_partial(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     and unnormalised accumulator, split-major) written to ``workspace``.
     Returns ``(workspace, splits_used)``."""
     B, Hq, Hkv, S, D = _check_decode_inputs(q, k_cache, v_cache)
-    lens_t = _as_int32(kv_len, B, k_cache.device) if isinstance(kv_len, torch.Tensor) else \
-        _as_int32([int(v) for v in (kv_len if hasattr(kv_len, "__len__") else [kv_len] * B)], B, k_cache.device)
-    mkl = S if max_kv_len is None else int(max_kv_len)
+    lens_t, mkl = _lengths(kv_len, max_kv_len, B, S, k_cache.device)
     plan_len = S if mkl <= 0 else min(mkl, S)
     if num_splits > 0:
         chunk = -(-plan_len // num_splits)

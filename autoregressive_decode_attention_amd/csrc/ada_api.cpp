@@ -172,7 +172,7 @@ int prepare_decode(const void* q, const void* k_cache, const void* v_cache, cons
   if (num_splits < 0 || num_splits > ADA_MAX_SPLITS) return ADA_ERR_SPLITS;
   if (batch > 65535 || n_kv_head > 65535) return ADA_ERR_SHAPE;  // grid limits
   if (batch == 0) return ADA_OK;
-  if (!q || !k_cache || !v_cache || !kv_len) return ADA_ERR_NULL;
+  if (!q || !k_cache || !v_cache) return ADA_ERR_NULL;  // kv_len may be NULL (lockstep rows)
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return ADA_ERR_ALIGN;
 
   Plan plan{};

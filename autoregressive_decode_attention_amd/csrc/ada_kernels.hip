@@ -204,8 +204,13 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   const int grp = lane / L;   // row of this lane within a wave-wide load
   const int sub = lane % L;   // dims [8*sub, +8) (and [64 + 8*sub, +8) when L == 8)
 
-  int n = kv_len[b];
-  n = n < 0 ? 0 : (n > max_kv_len ? max_kv_len : n);
+  // kv_len == NULL: every row holds max_kv_len live slots (one position for
+  // the whole batch), and nothing is read before the K/V stream starts.
+  int n = max_kv_len;
+  if (kv_len != nullptr) {
+    n = kv_len[b];
+    n = n < 0 ? 0 : (n > max_kv_len ? max_kv_len : n);
+  }
   const int nsplit = (n + chunk - 1) / chunk;  // splits holding live slots
   const size_t out_row0 = (static_cast<size_t>(b) * n_head + static_cast<size_t>(g) * G) * D;
 

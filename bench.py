@@ -8,12 +8,16 @@ over kv_len slots. Each kv_len has its own cache, and steps rotate over 5 sets
 of caches (960 MiB) so that no call finds its K/V in the 256 MB Infinity Cache:
 the inputs sit in HBM when the timed region starts.
 
-Printed: one JSON line with the metric (achieved algorithmic GB/s over the
-timed steps), the decode kernel's roofline (algorithmic bytes / its average
-duration from HIP events around each launch, against 8 TB/s), the fp64 CPU
-oracle timed on a bounded sample of the same step, and, under "also", the
-per-kv_len figures and the long-context workload (batch 8, 32/8 heads, bf16,
-kv_len 32768, 1.07 GB per call).
+The timed region replays one HIP graph per step (the step's 9 kernels:
+3 x append, partial, combine); eager launches from Python are reported
+beside it. Printed: one JSON line with the metric (achieved algorithmic GB/s
+over the timed steps), the roofline of the dominant kernel (the split-KV
+partial: algorithmic bytes / its average duration over back-to-back launches
+bracketed by HIP events, with the host queued ahead so that launch cost does
+not count, against 8 TB/s), the fp64 CPU oracle timed on a bounded sample of
+the same step, and, under "also", the per-kv_len figures and the
+long-context workload (batch 8, 32/8 heads, bf16, kv_len 32768, 1.07 GB per
+call).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -41,6 +45,7 @@ import workloads as W  # noqa: E402
 METRIC = "q_len=1 GQA decode attention: µs/call and achieved HBM GB/s (% of peak)"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
 MALL_BYTES = 256 * 2**20
+SPIN_CYCLES = 100_000_000  # GPU-side spin (about 40 ms) that lets the host run ahead
 SWEEP = (1024, 4096, 8192)
 KERNEL_SOURCE = ROOT / "autoregressive_decode_attention_amd" / "csrc" / "ada_kernels.hip"
 PMC_SUMMARY = ROOT / "profiles" / "decode_kernel_mha_sweep_pmc.md"
@@ -117,32 +122,85 @@ class Sweep:
                       for n in SWEEP)
         self.ws = ada.new_workspace(ws_need, device)
 
-    def step(self, events=None):
-        """Append then decode at each kv_len; the decode is issued as its two
-        kernels (partial, combine) so that HIP events bracket the partial
-        kernel alone: events[j] = (before partial, after partial, after combine)."""
+    def step(self, set_index: int | None = None):
+        """Append then decode (partial + combine kernels) at each kv_len, on the
+        next cache set (or ``set_index``). Lengths are one host-side position per
+        call (batch 1), so the kernels read no length from the device."""
         ada = self.ada
-        row = self.caches[self.i % self.sets]
+        row = self.caches[(self.i if set_index is None else set_index) % self.sets]
         self.i += 1
         for j, n in enumerate(SWEEP):
             k, v = row[j]
             ada.kv_append(self.k_new, self.v_new, k, v, self.pos[j])
-            if events is not None:
-                events[j][0].record()
-            _, used = ada.decode_partial(self.q[j], k, v, self.lens[j], scale=self.scale, max_kv_len=n,
-                                         workspace=self.ws)
-            if events is not None:
-                events[j][1].record()
+            _, used = ada.decode_partial(self.q[j], k, v, None, scale=self.scale, max_kv_len=n, workspace=self.ws)
             ada.decode_combine(self.ws, used, self.out[j], self.shape.n_kv_head)
-            if events is not None:
-                events[j][2].record()
-        self.splits = used
+
+    def capture(self):
+        """One HIP graph per cache set holding a whole step (9 kernels)."""
+        self.graphs = []
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            for s in range(self.sets):  # warm the binding's caches outside capture
+                self.step(s)
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+        for s in range(self.sets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                self.step(s)
+            self.graphs.append(g)
+        torch.cuda.synchronize()
+
+    def replay(self):
+        self.graphs[self.i % self.sets].replay()
+        self.i += 1
+
+    def time_partials(self, iters: int) -> list:
+        """Average duration of the partial kernel per kv_len: ``iters`` launches
+        back to back (rotating cache sets), bracketed by HIP events on the
+        launching stream. A GPU-side spin queued first lets the host enqueue
+        every launch before the first one runs, so host launch cost does not
+        show up as gaps."""
+        ada = self.ada
+        res = []
+        for j, n in enumerate(SWEEP):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(SPIN_CYCLES)
+            a.record()
+            for i in range(iters):
+                k, v = self.caches[i % self.sets][j]
+                ada.decode_partial(self.q[j], k, v, None, scale=self.scale, max_kv_len=n, workspace=self.ws)
+            b.record()
+            torch.cuda.synchronize()
+            res.append(a.elapsed_time(b) * 1e3 / iters)
+        return res
+
+    def time_calls(self, iters: int) -> list:
+        """As time_partials, for whole decode calls (partial + combine)."""
+        ada = self.ada
+        res = []
+        for j, n in enumerate(SWEEP):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(SPIN_CYCLES)
+            a.record()
+            for i in range(iters):
+                k, v = self.caches[i % self.sets][j]
+                _, used = ada.decode_partial(self.q[j], k, v, None, scale=self.scale, max_kv_len=n,
+                                             workspace=self.ws)
+                ada.decode_combine(self.ws, used, self.out[j], self.shape.n_kv_head)
+            b.record()
+            torch.cuda.synchronize()
+            res.append(a.elapsed_time(b) * 1e3 / iters)
+        return res
 
 
 def time_long_context(ada, device, iters: int = 20) -> dict:
     """The long-context workload (1.07 GB per call, 4x the Infinity Cache, so
-    every call streams from HBM): HIP events around each partial kernel and
-    around each whole call (partial + combine)."""
+    every call streams from HBM): average partial-kernel and whole-call
+    durations over back-to-back launches bracketed by HIP events."""
     wl = W.WORKLOADS["long_context"]
     shp = wl.shape
     x = W.decode_inputs(shp, [shp.capacity] * shp.batch, W.seed_for(4), device=device, tail="random",
@@ -153,35 +211,33 @@ def time_long_context(ada, device, iters: int = 20) -> dict:
     out = torch.empty_like(x["q"])
     scale = 1.0 / math.sqrt(D)
 
-    def call(ev=None):
-        if ev:
-            ev[0].record()
-        _, used = ada.decode_partial(x["q"], x["k_cache"], x["v_cache"], x["kv_len"], scale=scale,
-                                     max_kv_len=shp.capacity, workspace=ws)
-        if ev:
-            ev[1].record()
-        ada.decode_combine(ws, used, out, Hkv)
-        if ev:
-            ev[2].record()
+    def partial():
+        return ada.decode_partial(x["q"], x["k_cache"], x["v_cache"], None, scale=scale,
+                                  max_kv_len=shp.capacity, workspace=ws)[1]
 
-    for _ in range(5):
-        call()
-    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(iters)]
-    torch.cuda.synchronize()
-    for ev in evs:
-        call(ev)
-    torch.cuda.synchronize()
-    part = sorted(e[0].elapsed_time(e[1]) * 1e3 for e in evs)
-    whole = sorted(e[0].elapsed_time(e[2]) * 1e3 for e in evs)
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(SPIN_CYCLES)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / iters
+
+    for _ in range(3):
+        ada.decode_combine(ws, partial(), out, Hkv)
+    part = timed(partial)
+    whole = timed(lambda: ada.decode_combine(ws, partial(), out, Hkv))
     nbytes = decode_bytes(B, Hq, Hkv, D, [shp.capacity] * B)
-    med = lambda v: v[len(v) // 2]
     del x
     return {"workload": "long_context: batch 8, 32/8 heads, head_dim 128, bf16, kv_len 32768, 1% keys x8",
             "bytes_per_call": nbytes, "splits": splits,
-            "partial_us_median": round(med(part), 2), "partial_GBs": round(nbytes / med(part) / 1e3, 1),
-            "partial_frac_of_peak": round(nbytes / med(part) / 1e3 / PEAK_HBM_GBS, 4),
-            "call_us_median": round(med(whole), 2), "call_GBs": round(nbytes / med(whole) / 1e3, 1),
-            "call_frac_of_peak": round(nbytes / med(whole) / 1e3 / PEAK_HBM_GBS, 4)}
+            "partial_us": round(part, 2), "partial_GBs": round(nbytes / part / 1e3, 1),
+            "partial_frac_of_peak": round(nbytes / part / 1e3 / PEAK_HBM_GBS, 4),
+            "call_us": round(whole, 2), "call_GBs": round(nbytes / whole / 1e3, 1),
+            "call_frac_of_peak": round(nbytes / whole / 1e3 / PEAK_HBM_GBS, 4)}
 
 
 def cpu_baseline(seconds: float) -> dict:
@@ -232,37 +288,46 @@ def main(argv=None):
     device = torch.device("cuda", 0)
     torch.cuda.set_device(device)
     sweep = Sweep(ada, device)
+    launch = "hip_graph"
+    try:
+        sweep.capture()
+    except Exception as exc:  # graph capture unavailable: time eager launches instead
+        launch = f"eager ({type(exc).__name__})"
+        sweep.graphs = None
+    run_step = sweep.replay if sweep.graphs else sweep.step
     for _ in range(args.warmup):
-        sweep.step()
-    events = [[tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in SWEEP]
-              for _ in range(args.steps)]
+        run_step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        sweep.step(events[k])
+    for _ in range(args.steps):
+        run_step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = sweep.step_bytes / (ms_per_step * 1e-3) / 1e9
 
+    # Eager steps (every kernel launched from Python through the C ABI).
+    torch.cuda.synchronize()
+    e0 = time.perf_counter()
+    for _ in range(args.steps):
+        sweep.step()
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - e0) * 1e3 / args.steps
+
+    part_us = sweep.time_partials(args.steps)
+    call_us = sweep.time_calls(args.steps)
     per_kv = []
-    part_us_total = 0.0
-    part_bytes_total = 0
     for j, n in enumerate(SWEEP):
-        part = [events[k][j][0].elapsed_time(events[k][j][1]) * 1e3 for k in range(args.steps)]
-        whole = [events[k][j][0].elapsed_time(events[k][j][2]) * 1e3 for k in range(args.steps)]
-        pm, wm = sum(part) / len(part), sum(whole) / len(whole)
-        part_us_total += pm
-        part_bytes_total += sweep.decode_bytes[j]
         nb = sweep.decode_bytes[j]
         per_kv.append({"kv_len": n, "bytes": nb, "splits": ada.decode_num_splits(1, 16, n),
-                       "partial_us_mean": round(pm, 2), "partial_GBs": round(nb / pm / 1e3, 1),
-                       "call_us_mean": round(wm, 2), "call_us_median": round(sorted(whole)[len(whole) // 2], 2),
-                       "call_GBs": round(nb / wm / 1e3, 1), "call_frac_of_peak": round(nb / wm / 1e3 / PEAK_HBM_GBS, 4)})
-    achieved = part_bytes_total / part_us_total / 1e3
+                       "partial_us": round(part_us[j], 2), "partial_GBs": round(nb / part_us[j] / 1e3, 1),
+                       "call_us": round(call_us[j], 2), "call_GBs": round(nb / call_us[j] / 1e3, 1),
+                       "call_frac_of_peak": round(nb / call_us[j] / 1e3 / PEAK_HBM_GBS, 4)})
+    achieved = sum(sweep.decode_bytes) / sum(part_us) / 1e3
     traffic = pmc_traffic()
 
-    also = {"per_kv_len": per_kv}
+    also = {"per_kv_len": per_kv, "eager_ms_per_step": round(eager_ms, 4),
+            "eager_GBs": round(sweep.step_bytes / (eager_ms * 1e-3) / 1e9, 1)}
     if not args.no_long_context:
         also["long_context"] = time_long_context(ada, device)
 
@@ -273,12 +338,12 @@ def main(argv=None):
         "config": {"workload": "mha_sweep: one-token decode, batch 1, 16 heads = 16 KV heads, head_dim 128, fp16, "
                                "kv_len 1024/4096/8192 (append + decode each), capacity 8192, "
                                f"cold caches rotated over {sweep.sets} sets",
-                   "step_bytes": sweep.step_bytes, "calls_per_step": 6},
+                   "step_bytes": sweep.step_bytes, "kernels_per_step": 9, "launch": launch},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "partial_kernel (split-KV partial of the decode; the combine kernel follows it)",
                      "bytes_per_launch": sweep.decode_bytes,
-                     "us_per_launch": [p["partial_us_mean"] for p in per_kv]},
+                     "us_per_launch": [round(u, 2) for u in part_us]},
         "also": also,
     }
     if not args.no_cpu_baseline:

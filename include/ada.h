@@ -139,7 +139,11 @@ size_t ada_decode_workspace_bytes(int batch, int n_head, int n_kv_head, int head
  *   k_cache,   device, [batch, n_kv_head, capacity, head_dim]; only slots
  *   v_cache    j < n_b are read, n_b = min(max(kv_len[b], 0), max_kv_len).
  *              Slots at and beyond n_b may hold anything (NaN included).
- *   kv_len     device int32 [batch], live prefix length per batch row.
+ *   kv_len     device int32 [batch], live prefix length per batch row, or
+ *              NULL: every row then holds max_kv_len live slots (one host-side
+ *              position for the whole batch, as the pages' decode loops pass
+ *              it, [ACTIVE-PREFIX] section 2), and the kernels read no length
+ *              from the device.
  *   max_kv_len host upper bound on kv_len[b], sizes the launch; <= 0 means
  *              capacity; > capacity is ADA_ERR_SHAPE. Device values above it
  *              are clamped to it.

@@ -76,7 +76,7 @@ def decode(ada, q=P, k=P2, v=P3, lens=P4, B=1, Hq=32, Hkv=8, D=128, S=2048, mkl=
     (dict(q=NUL), -1),
     (dict(k=NUL), -1),
     (dict(v=NUL), -1),
-    (dict(lens=NUL), -1),
+    (dict(lens=NUL, out=NUL), -1),     # NULL lengths are the lockstep form; NULL out is not
     (dict(out=NUL), -1),
     (dict(B=-1), -2),
     (dict(Hq=0), -2),
@@ -131,7 +131,7 @@ def test_partial_and_combine_validation(ada):
                          kw.get("ws", NUL), kw.get("ws_bytes", 0), ctypes.byref(used), NUL]
     assert part(*args(dtype=3)) == -4
     assert part(*args(q=NUL)) == -1
-    assert part(*args(lens=NUL)) == -1
+    assert part(*args(lens=NUL)) == -7                # NULL lengths are valid (lockstep); workspace missing
     assert part(*args(D=96)) == -5
     assert part(*args(scale=float("-inf"))) == -6
     assert part(*args(splits=300)) == -8

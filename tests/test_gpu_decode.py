@@ -414,3 +414,21 @@ def test_key_ranges_merged_by_combine(ada, ora):
     ada.decode_combine(merged, total, out, n_kv_head=Hkv)
     want = ora.decode(x["q"], x["k_cache"], x["v_cache"], lens, SCALE)
     assert_parity(out, want, "fp16", "key ranges merged")
+
+
+def test_lockstep_lengths_from_the_host(ada, ora):
+    """One host-side position for the whole batch ([ACTIVE-PREFIX] section 2:
+    the length comes from a host int, no device read): NULL device lengths."""
+    shp = shape(4, 32, 8, 5000, "bf16")
+    for n, splits in ((4321, 0), (1, 0), (700, 3), (5000, 1)):
+        x = W.decode_inputs(shp, [n] * 4, 718 + n, tail="nan")
+        d = gpu(x)
+        out = ada.decode_attn_gqa_ex(d["q"], d["k_cache"], d["v_cache"], n, scale=SCALE, num_splits=splits)
+        out2 = ada.decode_attn_gqa_ex(d["q"], d["k_cache"], d["v_cache"], None, scale=SCALE, max_kv_len=n,
+                                      num_splits=splits)
+        assert torch.equal(out, out2)
+        want = ora.decode(x["q"], x["k_cache"], x["v_cache"], [n] * 4, SCALE)
+        assert_parity(out, want, "bf16", f"lockstep n={n}")
+    x = gpu(W.decode_inputs(shp, [0] * 4, 719, tail="nan"))
+    out = ada.decode_attn_gqa(x["q"], x["k_cache"], x["v_cache"], 0, scale=SCALE)
+    assert torch.count_nonzero(out) == 0
