@@ -70,7 +70,7 @@ def _declare(lib):
         "ada_device_num_cus": ([c_int, ctypes.POINTER(c_int)], c_int),
         "ada_kv_append": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                            c_int, c_void_p], c_int),
-        "ada_decode_num_splits": ([c_int, c_int, c_int, c_int], c_int),
+        "ada_decode_num_splits": ([c_int, c_int, c_int, c_int, c_int], c_int),
         "ada_decode_workspace_bytes": ([c_int, c_int, c_int, c_int, c_int], c_size_t),
         "ada_decode_attn_gqa": (decode_args, c_int),
         "ada_decode_attn_gqa_ex": (decode_args + [c_int], c_int),
@@ -137,10 +137,10 @@ def _cus(device: torch.device) -> int:
     return _CUS[idx]
 
 
-def decode_num_splits(batch: int, n_kv_head: int, max_kv_len: int, num_cus: int | None = None) -> int:
+def decode_num_splits(batch: int, n_head: int, n_kv_head: int, max_kv_len: int, num_cus: int | None = None) -> int:
     if num_cus is None:
         num_cus = _cus(torch.device("cuda", torch.cuda.current_device()))
-    return int(_lib.ada_decode_num_splits(int(batch), int(n_kv_head), int(max_kv_len), int(num_cus)))
+    return int(_lib.ada_decode_num_splits(int(batch), int(n_head), int(n_kv_head), int(max_kv_len), int(num_cus)))
 
 
 def decode_workspace_bytes(batch: int, n_head: int, n_kv_head: int, head_dim: int, num_splits: int) -> int:
@@ -256,7 +256,7 @@ def decode_attn_gqa_ex(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
         chunk = -(-plan_len // num_splits)
         splits = -(-plan_len // chunk)
     else:
-        splits = decode_num_splits(B, Hkv, plan_len)
+        splits = decode_num_splits(B, Hq, Hkv, plan_len)
     need = decode_workspace_bytes(B, Hq, Hkv, D, splits) if splits > 1 else 0
     ws = workspace if workspace is not None else _workspace(k_cache.device, need)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
@@ -304,7 +304,7 @@ def decode_partial(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
         chunk = -(-plan_len // num_splits)
         splits = -(-plan_len // chunk)
     else:
-        splits = decode_num_splits(B, Hkv, plan_len)
+        splits = decode_num_splits(B, Hq, Hkv, plan_len)
     if workspace is None:
         workspace = new_workspace(decode_workspace_bytes(B, Hq, Hkv, D, splits), k_cache.device)
     used = ctypes.c_int(0)

@@ -64,17 +64,23 @@ Plan forced_plan(int max_kv_len, int requested) {
   return {static_cast<int>(ceil_div(max_kv_len, chunk)), chunk};
 }
 
-// Heuristic: about two 4-wave workgroups per compute unit, every split at
-// least 128 slots, ranges rounded up to whole 64-slot tiles.
-Plan heuristic_plan(int batch, int n_kv_head, int max_kv_len, int num_cus) {
-  if (batch <= 0 || n_kv_head <= 0 || max_kv_len <= 0 || num_cus <= 0) return {1, max_kv_len > 0 ? max_kv_len : 1};
+// Heuristic (measured on MI355X, cold HBM): one 4-wave workgroup per compute
+// unit for grouped heads (G >= 2: their key-row work keeps the SIMDs busy),
+// two for G == 1; splits never shorter than 64 slots (one workgroup tile);
+// while a split would exceed 4096 slots, double the split count so long rows
+// still spread over every compute unit. Ranges are rounded up to whole
+// 64-slot tiles.
+Plan heuristic_plan(int batch, int n_head, int n_kv_head, int max_kv_len, int num_cus) {
+  if (batch <= 0 || n_head <= 0 || n_kv_head <= 0 || max_kv_len <= 0 || num_cus <= 0)
+    return {1, max_kv_len > 0 ? max_kv_len : 1};
   const int64_t units = static_cast<int64_t>(batch) * n_kv_head;
-  const int64_t target_wgs = 2 * static_cast<int64_t>(num_cus);
-  int64_t splits = ceil_div(target_wgs, units);
-  const int64_t by_len = ceil_div(max_kv_len, 128);
+  const int64_t per_cu = n_head == n_kv_head ? 2 : 1;
+  int64_t splits = ceil_div(per_cu * num_cus, units);
+  const int64_t by_len = ceil_div(max_kv_len, ada::kTileRows);
   if (splits > by_len) splits = by_len;
-  if (splits > ADA_MAX_SPLITS) splits = ADA_MAX_SPLITS;
   if (splits < 1) splits = 1;
+  while (ceil_div(max_kv_len, splits) > 4096 && splits * 2 <= by_len) splits *= 2;
+  if (splits > ADA_MAX_SPLITS) splits = ADA_MAX_SPLITS;
   int64_t chunk = ceil_div(ceil_div(max_kv_len, splits), ada::kTileRows) * ada::kTileRows;
   return {static_cast<int>(ceil_div(max_kv_len, chunk)), static_cast<int>(chunk)};
 }
@@ -128,8 +134,8 @@ int ada_device_num_cus(int device, int* num_cus) {
   return ADA_OK;
 }
 
-int ada_decode_num_splits(int batch, int n_kv_head, int max_kv_len, int num_cus) {
-  return heuristic_plan(batch, n_kv_head, max_kv_len, num_cus).splits;
+int ada_decode_num_splits(int batch, int n_head, int n_kv_head, int max_kv_len, int num_cus) {
+  return heuristic_plan(batch, n_head, n_kv_head, max_kv_len, num_cus).splits;
 }
 
 size_t ada_decode_workspace_bytes(int batch, int n_head, int n_kv_head, int head_dim, int num_splits) {
@@ -182,7 +188,7 @@ int prepare_decode(const void* q, const void* k_cache, const void* v_cache, cons
     int cus = 0;
     int rc = current_device_cus(&cus);
     if (rc != ADA_OK) return rc;
-    plan = heuristic_plan(batch, n_kv_head, max_kv_len, cus);
+    plan = heuristic_plan(batch, n_head, n_kv_head, max_kv_len, cus);
   }
   *p = ada::DecodeLaunch{};
   p->q = q;

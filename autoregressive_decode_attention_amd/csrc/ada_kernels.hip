@@ -21,13 +21,15 @@
 //   * Lane layout: L lanes per key row (8 for G <= 4, 16 above), each lane
 //     holding 8 or 16 head dims in 16-byte chunks, so one 16-byte load per
 //     lane covers 64 / L consecutive rows in contiguous 128- or 256-byte
-//     runs: fully coalesced. Loads run P tiles ahead of the compute through a
-//     register ring.
+//     runs: fully coalesced, with the nontemporal cache policy (each byte is
+//     read once). Loads run P tiles ahead of the compute through a register
+//     ring.
 //   * q.k in fp32 with the packed 16-bit dot instructions (products of two
 //     16-bit values are exact in fp32), summed over the L lanes of a row with
 //     DPP butterfly adds; scale*log2(e) is applied to the sum.
-//   * Online softmax in base 2 per lane group (running max m, sum l, fp32
-//     accumulator), rescaling only when a running maximum grows; lane groups
+//   * Online softmax in base 2 per lane group (reference max m, sum l, fp32
+//     accumulator), rescaling only when a score exceeds the reference by
+//     more than 2^8 (so almost never after the first rows); lane groups
 //     are merged with DPP and the 16/32-lane permlane swaps, wavefronts
 //     through LDS.
 //   * With one split the workgroup writes the output directly. With several
@@ -55,6 +57,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = kThreads / 64;
 constexpr float kNegInf = -__builtin_inff();
+// Largest base-2 exponent a softmax weight may reach before the accumulator
+// is rescaled (weights stay <= 256, sums stay far inside fp32 range).
+constexpr float kRescaleSlack = 8.0f;
 
 struct F16 {
   static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -153,6 +158,15 @@ __device__ __forceinline__ float finite_ref(float m) { return m == kNegInf ? 0.0
 
 __device__ __forceinline__ uint4 load16(const uint16_t* p) {
   return *reinterpret_cast<const uint4*>(p);
+}
+
+// K/V rows are read exactly once: nontemporal loads (the `nt` cache policy)
+// stream them past the caches. On MI355X a plain read kernel reaches about
+// 6.4 TB/s with ordinary loads and about 7.2 TB/s with nontemporal ones.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_stream(const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 template <class E>
@@ -264,8 +278,8 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
       const size_t off = static_cast<size_t>(r) * D;
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        kr[t][c] = load16(kbase + off + 64 * c);
-        vr[t][c] = load16(vbase + off + 64 * c);
+        kr[t][c] = load16_stream(kbase + off + 64 * c);
+        vr[t][c] = load16_stream(vbase + off + 64 * c);
       }
     }
   };
@@ -284,7 +298,10 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
         x[t][i] = valid ? s * scale_log2 : kNegInf;
       }
     }
-    // Rescale only when some lane group's running maximum grows.
+    // The reference m need not be the exact running maximum: weights
+    // exp2(x - m) up to 2^kRescaleSlack are harmless in fp32, so the
+    // accumulator is rescaled only when some lane group sees a score more
+    // than kRescaleSlack above its reference (always on its first live row).
     float mt[G];
     bool grow = false;
 #pragma unroll
@@ -292,7 +309,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
       mt[i] = x[0][i];
 #pragma unroll
       for (int t = 1; t < T; ++t) mt[i] = fmaxf(mt[i], x[t][i]);
-      grow |= mt[i] > m[i];
+      grow |= mt[i] > m[i] + kRescaleSlack;
     }
     if (__any(grow)) {
 #pragma unroll
@@ -395,111 +412,72 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   }
 }
 
-// Combine kernel: one workgroup per (KV head, batch row) merges the
-// num_splits partials of the row's G heads, in split order, with log-sum-exp
-// weights:
-//   M = max_s m_s, w_s = exp2(m_s - M) / sum_s exp2(m_s - M) l_s,
-//   out = sum_s w_s acc_s,
+// Combine kernel: one workgroup per (KV head, batch row), one wavefront per
+// query head of the group, two dims per lane. It merges the num_splits
+// partials of its head in split order with log-sum-exp weights,
+//   M = max_s m_s,  out = sum_s exp2(m_s - M) acc_s / sum_s exp2(m_s - M) l_s,
 // then rounds to the output type. Empty splits carry m = -inf and weigh 0
-// (their accumulators are never used); a row whose splits are all empty
-// (kv_len 0) gets zeros. kv_len is not read: the marks say everything.
+// (their accumulators are never read); a head whose splits are all empty
+// (kv_len 0) gets zeros.
 //
-// Column = 4 consecutive dims of one head; R threads share a column and take
-// every R-th split. The first batch of accumulator loads is issued together
-// with the (m, l) loads, so the workgroup waits for memory once.
-template <class E, int G>
-__global__ __launch_bounds__(kThreads) void combine_kernel(
+// Splits are taken in batches of kBatch whose loads are all issued before
+// any is used, and batches are merged online (running max, rescaled sums),
+// so a call waits for memory about once per batch and needs no LDS or
+// barrier.
+template <class E>
+__global__ __launch_bounds__(64 * kMaxGroup) void combine_kernel(
     uint16_t* __restrict__ out, const float2* __restrict__ part_ml,
-    const float* __restrict__ part_acc, int n_kv_head, int num_splits) {
+    const float* __restrict__ part_acc, int n_kv_head, int group, int num_splits) {
   constexpr int D = kHeadDim;
-  constexpr int kCols = G * (D / 4);
-  constexpr int R = kThreads / kCols;
-  constexpr int kBatch = 8;
+  constexpr int kBatch = 16;
   const int g = blockIdx.x;
   const int b = blockIdx.y;
-  const int n_head = n_kv_head * G;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int ns = num_splits;
-
-  __shared__ float2 s_pml[G][kMaxSplits];
-  __shared__ float4 s_red[R > 1 ? R : 1][kCols];
-  const size_t out_row0 = (static_cast<size_t>(b) * n_head + static_cast<size_t>(g) * G) * D;
-  const size_t head_row0 = static_cast<size_t>(b) * n_head + static_cast<size_t>(g) * G;
+  const int lane = threadIdx.x & 63;
+  const int i = threadIdx.x >> 6;  // query head within the group
+  const int n_head = n_kv_head * group;
+  const size_t head_row = static_cast<size_t>(b) * n_head + static_cast<size_t>(g) * group + i;
   const size_t split_stride = static_cast<size_t>(gridDim.y) * n_head;  // split-major partials
-  const int col = tid % kCols;
-  const int r = tid / kCols;
-  const bool active = r < R;
-  const int ci = col / (D / 4);
-  const int cd = (col % (D / 4)) * 4;
-  const float4* acc4 = reinterpret_cast<const float4*>(part_acc);
-  const size_t col_row0 = head_row0 + ci;
+  const float2* acc2 = reinterpret_cast<const float2*>(part_acc);
 
-  float4 av[kBatch];
-#pragma unroll
-  for (int k = 0; k < kBatch; ++k) {
-    const int s = r + k * R;
-    if (active && s < ns) av[k] = acc4[((col_row0 + s * split_stride) * D + cd) / 4];
-  }
-  for (int e = tid; e < G * ns; e += kThreads) {
-    const int i = e / ns;
-    const int s = e % ns;
-    s_pml[i][s] = part_ml[head_row0 + i + s * split_stride];
-  }
-  __syncthreads();
-  // Per head (one wave per head): maximum and normaliser over the splits,
-  // then each split's weight exp2(m_s - M) / L, stored in place of its m.
-  for (int i = wave; i < G; i += kWaves) {
-    float mx = kNegInf;
-    for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, s_pml[i][s].x);
-    mx = wave_reduce<Max>(mx);
-    const float ref = finite_ref(mx);
-    float ls = 0.0f;
-    for (int s = lane; s < ns; s += 64) ls += s_pml[i][s].y * fast_exp2(s_pml[i][s].x - ref);
-    ls = wave_reduce<Sum>(ls);
-    const float inv = ls > 0.0f ? 1.0f / ls : 0.0f;
-    for (int s = lane; s < ns; s += 64) s_pml[i][s].x = fast_exp2(s_pml[i][s].x - ref) * inv;
-  }
-  __syncthreads();
-  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto add = [&](float w, const float4& a) {
-    if (w > 0.0f) {  // empty splits (w == 0) hold stale accumulators: skip, never multiply
-      o.x = fmaf(w, a.x, o.x);
-      o.y = fmaf(w, a.y, o.y);
-      o.z = fmaf(w, a.z, o.z);
-      o.w = fmaf(w, a.w, o.w);
-    }
-  };
-  if (active) {
+  float m_run = kNegInf, l_run = 0.0f;
+  float2 o = make_float2(0.0f, 0.0f);
+  for (int s0 = 0; s0 < num_splits; s0 += kBatch) {
+    float2 ml[kBatch], a[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int s = r + k * R;
-      if (s < ns) add(s_pml[ci][s].x, av[k]);
-    }
-    for (int s = r + kBatch * R; s < ns; s += R) {
-      const float w = s_pml[ci][s].x;
-      if (w > 0.0f) add(w, acc4[((col_row0 + s * split_stride) * D + cd) / 4]);
-    }
-    if (R > 1) s_red[r][col] = o;
-  }
-  if (R > 1) {
-    __syncthreads();
-    if (r == 0) {
-      for (int k = 1; k < R; ++k) {
-        const float4 a = s_red[k][col];
-        o.x += a.x;
-        o.y += a.y;
-        o.z += a.z;
-        o.w += a.w;
+      const int s = s0 + k;
+      if (s < num_splits) {
+        const size_t row = head_row + static_cast<size_t>(s) * split_stride;
+        ml[k] = part_ml[row];
+        a[k] = acc2[row * (D / 2) + lane];
+      } else {
+        ml[k] = make_float2(kNegInf, 0.0f);
+        a[k] = make_float2(0.0f, 0.0f);
       }
     }
+    float mb = m_run;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) mb = fmaxf(mb, ml[k].x);
+    const float ref = finite_ref(mb);
+    const float c = fast_exp2(m_run - ref);  // rescale what earlier batches summed
+    l_run *= c;
+    o.x *= c;
+    o.y *= c;
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const float w = fast_exp2(ml[k].x - ref);
+      if (w > 0.0f) {  // empty splits (w == 0) hold stale accumulators: skip, never multiply
+        l_run = fmaf(w, ml[k].y, l_run);
+        o.x = fmaf(w, a[k].x, o.x);
+        o.y = fmaf(w, a[k].y, o.y);
+      }
+    }
+    m_run = mb;
   }
-  if (r == 0) {
-    const uint32_t lo = static_cast<uint32_t>(E::round(o.x)) | (static_cast<uint32_t>(E::round(o.y)) << 16);
-    const uint32_t hi = static_cast<uint32_t>(E::round(o.z)) | (static_cast<uint32_t>(E::round(o.w)) << 16);
-    *reinterpret_cast<uint2*>(out + out_row0 + static_cast<size_t>(ci) * D + cd) = make_uint2(lo, hi);
-  }
+  const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+  const uint32_t packed = static_cast<uint32_t>(E::round(o.x * inv)) |
+                          (static_cast<uint32_t>(E::round(o.y * inv)) << 16);
+  reinterpret_cast<uint32_t*>(out + head_row * D)[lane] = packed;
 }
 
 // In-place append: row pos[b] of every KV head of batch row b, K and V, as
@@ -556,13 +534,19 @@ hipError_t launch_partial_g(const DecodeLaunch& p) {
   return hipGetLastError();
 }
 
-template <class E, int G>
-hipError_t launch_combine_g(const CombineLaunch& p) {
+hipError_t launch_combine_impl(const CombineLaunch& p) {
   const WorkspaceLayout w = workspace_layout(p.batch, p.n_head, p.n_kv_head, kHeadDim, p.splits);
   const char* base = static_cast<const char*>(p.workspace);
-  hipLaunchKernelGGL((combine_kernel<E, G>), dim3(p.n_kv_head, p.batch), dim3(kThreads), 0, p.stream,
-                     static_cast<uint16_t*>(p.out), reinterpret_cast<const float2*>(base + w.ml_offset),
-                     reinterpret_cast<const float*>(base + w.acc_offset), p.n_kv_head, p.splits);
+  const int group = p.n_head / p.n_kv_head;
+  const float2* ml = reinterpret_cast<const float2*>(base + w.ml_offset);
+  const float* acc = reinterpret_cast<const float*>(base + w.acc_offset);
+  uint16_t* out = static_cast<uint16_t*>(p.out);
+  const dim3 grid(p.n_kv_head, p.batch), block(64 * group);
+  if (p.dtype == 1) {
+    hipLaunchKernelGGL(combine_kernel<BF16>, grid, block, 0, p.stream, out, ml, acc, p.n_kv_head, group, p.splits);
+  } else {
+    hipLaunchKernelGGL(combine_kernel<F16>, grid, block, 0, p.stream, out, ml, acc, p.n_kv_head, group, p.splits);
+  }
   return hipGetLastError();
 }
 
@@ -583,7 +567,7 @@ hipError_t launch_combine_g(const CombineLaunch& p) {
 
 hipError_t launch_partial(const DecodeLaunch& p) { ADA_DISPATCH_GROUP(launch_partial_g, p) }
 
-hipError_t launch_combine(const CombineLaunch& p) { ADA_DISPATCH_GROUP(launch_combine_g, p) }
+hipError_t launch_combine(const CombineLaunch& p) { return launch_combine_impl(p); }
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             const int32_t* pos, int batch, int n_kv_head, int capacity,

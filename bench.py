@@ -45,6 +45,7 @@ import workloads as W  # noqa: E402
 METRIC = "q_len=1 GQA decode attention: µs/call and achieved HBM GB/s (% of peak)"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E peak
 MALL_BYTES = 256 * 2**20
+CALIB_BYTES = 256 * 2**20  # calibration copy for the counter runs
 SPIN_CYCLES = 100_000_000  # GPU-side spin (about 40 ms) that lets the host run ahead
 SWEEP = (1024, 4096, 8192)
 KERNEL_SOURCE = ROOT / "autoregressive_decode_attention_amd" / "csrc" / "ada_kernels.hip"
@@ -118,7 +119,7 @@ class Sweep:
         self.decode_bytes = [decode_bytes(B, Hq, Hkv, D, [n]) for n in SWEEP]
         self.step_bytes = sum(self.decode_bytes) + 3 * append_bytes(B, Hkv, D)
         self.i = 0
-        ws_need = max(ada.decode_workspace_bytes(B, Hq, Hkv, D, max(2, ada.decode_num_splits(B, Hkv, n)))
+        ws_need = max(ada.decode_workspace_bytes(B, Hq, Hkv, D, max(2, ada.decode_num_splits(B, Hq, Hkv, n)))
                       for n in SWEEP)
         self.ws = ada.new_workspace(ws_need, device)
 
@@ -206,7 +207,7 @@ def time_long_context(ada, device, iters: int = 20) -> dict:
     x = W.decode_inputs(shp, [shp.capacity] * shp.batch, W.seed_for(4), device=device, tail="random",
                         outlier_p=wl.outlier_p, outlier_scale=wl.outlier_scale)
     B, Hq, Hkv, D = shp.batch, shp.n_head, shp.n_kv_head, shp.head_dim
-    splits = ada.decode_num_splits(B, Hkv, shp.capacity)
+    splits = ada.decode_num_splits(B, Hq, Hkv, shp.capacity)
     ws = ada.new_workspace(ada.decode_workspace_bytes(B, Hq, Hkv, D, max(2, splits)), device)
     out = torch.empty_like(x["q"])
     scale = 1.0 / math.sqrt(D)
@@ -287,6 +288,14 @@ def main(argv=None):
 
     device = torch.device("cuda", 0)
     torch.cuda.set_device(device)
+    # A plain copy of known size (256 MiB read, 256 MiB written): the reference
+    # that scales the FETCH_SIZE / WRITE_SIZE counters of the profiled runs.
+    calib_src = torch.empty(CALIB_BYTES // 2, dtype=torch.float16, device=device).fill_(1.0)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
+
     sweep = Sweep(ada, device)
     launch = "hip_graph"
     try:
@@ -319,7 +328,7 @@ def main(argv=None):
     per_kv = []
     for j, n in enumerate(SWEEP):
         nb = sweep.decode_bytes[j]
-        per_kv.append({"kv_len": n, "bytes": nb, "splits": ada.decode_num_splits(1, 16, n),
+        per_kv.append({"kv_len": n, "bytes": nb, "splits": ada.decode_num_splits(1, 16, 16, n),
                        "partial_us": round(part_us[j], 2), "partial_GBs": round(nb / part_us[j] / 1e3, 1),
                        "call_us": round(call_us[j], 2), "call_GBs": round(nb / call_us[j] / 1e3, 1),
                        "call_frac_of_peak": round(nb / call_us[j] / 1e3 / PEAK_HBM_GBS, 4)})

@@ -105,12 +105,14 @@ int ada_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_c
  * Split heuristic: number of key-range splits for a decode call over
  * batch * n_kv_head (batch row, KV head) units whose live prefixes are at
  * most max_kv_len slots, on a device with num_cus compute units. It aims at
- * two 4-wave workgroups per compute unit without splitting prefixes below
- * 128 slots, and returns the split count after rounding the per-split slot
- * range up to a multiple of 64. Pure host arithmetic; returns >= 1 (1 for
- * non-positive inputs).
+ * one 4-wave workgroup per compute unit when query heads are grouped
+ * (n_head > n_kv_head) and two otherwise, never splits below 64 slots, and
+ * doubles the split count while a split would exceed 4096 slots; the
+ * per-split range is rounded up to a multiple of 64 and the count returned
+ * is the one that rounding yields. Pure host arithmetic; returns 1..256
+ * (1 for non-positive inputs).
  */
-int ada_decode_num_splits(int batch, int n_kv_head, int max_kv_len, int num_cus);
+int ada_decode_num_splits(int batch, int n_head, int n_kv_head, int max_kv_len, int num_cus);
 
 /*
  * Bytes of device workspace that holds num_splits (>= 1) per-split partial
@@ -188,11 +190,12 @@ int ada_decode_attn_gqa_ex(const void* q, const void* k_cache, const void* v_cac
  * ada_decode_partial: arguments as ada_decode_attn_gqa_ex without `out`;
  * always writes partials (never the output) for every split, the split count
  * it used going to *splits_used (may be NULL). Split s covers slots
- * [s*c, min((s+1)*c, n_b)) with c = ceil(max_kv_len / splits); its entry
- * holds m = max of scale*log2(e)*q.k over that range, l = sum of
- * exp2(score - m), acc = sum of exp2(score - m) * v (fp32, unnormalised); an
- * empty range holds m = -inf, l = 0 and an accumulator that must not be
- * read. This is the online (running max and sum) softmax of
+ * [s*c, min((s+1)*c, n_b)) with c = ceil(max_kv_len / splits) (the
+ * heuristic rounds c up to a multiple of 64); with scores
+ * x = scale*log2(e)*q.k, its entry holds a reference m (max x - 8 <= m <=
+ * max x over the range), l = sum of exp2(x - m) and acc = sum of
+ * exp2(x - m) * v (fp32, unnormalised); an empty range holds m = -inf, l = 0
+ * and an accumulator that must not be read. This is the online (running max and sum) softmax of
  * [DECODE-FASTPATH], "Current limitation", applied per key range.
  *
  * ada_decode_combine: merges num_splits partials per (batch row, query head)

@@ -163,22 +163,31 @@ def test_workspace_bytes_arithmetic(ada):
 
 
 def test_split_heuristic_properties(ada):
-    # worked examples on a 256-CU device
-    assert ada.decode_num_splits(8, 8, 32768, 256) == 8      # long context: 64 units x 8 = 512 workgroups
-    assert ada.decode_num_splits(1, 16, 4096, 256) == 32     # MHA kv 4096: 128-slot splits
-    assert ada.decode_num_splits(1, 8, 400, 256) == 4        # tiny
+    ns = ada.decode_num_splits
+    # worked examples on a 256-CU device (the values the tuning sweeps favoured)
+    assert ns(8, 32, 8, 32768, 256) == 8     # long context: 4 splits would be 8192 slots -> doubled
+    assert ns(1, 16, 16, 4096, 256) == 32    # MHA kv 4096: two workgroups per CU, 128-slot splits
+    assert ns(1, 16, 16, 8192, 256) == 32
+    assert ns(1, 16, 16, 1024, 256) == 16    # capped by 64-slot splits
+    assert ns(4, 32, 8, 8192, 256) == 8      # MiniCPM shape: one workgroup per CU
+    assert ns(1, 32, 8, 400, 256) == 7       # tiny
+    assert ns(1, 32, 8, 235, 256) == 4
     for B in (1, 2, 4, 8, 16, 64):
-        for Hkv in (1, 8, 16):
-            for n in (1, 63, 64, 65, 400, 1258, 4096, 8191, 32768, 131072):
-                s = ada.decode_num_splits(B, Hkv, n, 256)
+        for Hq, Hkv in ((16, 16), (32, 8), (8, 1)):
+            for n in (1, 63, 64, 65, 400, 1258, 4096, 8191, 32768, 131072, 1 << 20):
+                s = ns(B, Hq, Hkv, n, 256)
                 assert 1 <= s <= 256
-                # every split holds at least one live slot and covers the range
                 chunk = -(-n // s)
-                assert -(-n // chunk) == s or s == 1
+                chunk = -(-chunk // 64) * 64
+                # the count is the one the 64-slot rounding yields, and every split is live
+                assert s == -(-n // chunk)
                 assert s <= max(1, -(-n // 64))
-                # never many more workgroups than two per CU once the batch fills the GPU
-                if B * Hkv >= 512:
-                    assert s == 1
-    assert ada.decode_num_splits(0, 8, 100, 256) == 1
-    assert ada.decode_num_splits(1, 8, 0, 256) == 1
-    assert ada.decode_num_splits(1, 8, 100, 0) == 1
+                # splits longer than 4096 slots only when the split count is at its cap
+                if chunk > 4096 + 63:
+                    assert s * 2 > -(-n // 64) or s * 2 > 256
+                # splitting never asks for more than two workgroups per CU unless rows are long
+                if s > 1 and B * Hkv * s > 2 * 256:
+                    assert chunk >= 2048
+    assert ns(0, 8, 8, 100, 256) == 1
+    assert ns(1, 8, 8, 0, 256) == 1
+    assert ns(1, 8, 8, 100, 0) == 1
