@@ -11,6 +11,7 @@ The functions keep the C names without the ``ada_`` prefix:
 * ``kv_append(k_new, v_new, k_cache, v_cache, pos)``
 * ``decode_attn_gqa(q, k_cache, v_cache, kv_len, scale=None, out=None, max_kv_len=None)``
 * ``decode_attn_gqa_ex(..., num_splits=...)``
+* ``decode_step(q, k_new, v_new, k_cache, v_cache, pos, ...)``: append + decode in one call
 * ``decode_partial(q, k_cache, v_cache, kv_len, ...)`` and
   ``decode_combine(workspace, num_splits, out, n_kv_head)``: the two halves
 * ``decode_num_splits``, ``decode_workspace_bytes``, ``device_num_cus``,
@@ -45,6 +46,7 @@ EXPORTS = (
     "ada_abi_version", "ada_status_string", "ada_last_hip_error", "ada_device_num_cus",
     "ada_kv_append", "ada_decode_num_splits", "ada_decode_workspace_bytes",
     "ada_decode_attn_gqa", "ada_decode_attn_gqa_ex", "ada_decode_partial", "ada_decode_combine",
+    "ada_decode_step",
 )
 
 
@@ -78,6 +80,8 @@ def _declare(lib):
                                 c_float, c_int, c_int, c_void_p, c_size_t, ctypes.POINTER(c_int), c_void_p], c_int),
         "ada_decode_combine": ([c_void_p, c_size_t, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p],
                                c_int),
+        "ada_decode_step": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
+                             c_int, c_int, c_float, c_int, c_void_p, c_void_p, c_size_t, c_void_p, c_int], c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -330,6 +334,49 @@ def decode_combine(workspace: torch.Tensor, num_splits: int, out: torch.Tensor, 
     return out
 
 
+def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor,
+                v_cache: torch.Tensor, pos, scale: float | None = None, out: torch.Tensor | None = None,
+                max_pos: int | None = None, num_splits: int = 0,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step in one call: write k_new/v_new [B, Hkv, D] at slot pos
+    of the caches, then attend over slots 0..pos (kv_len = pos + 1). ``pos``:
+    a host int (every row at that slot), host ints, or an int32 GPU tensor
+    (then ``max_pos`` bounds it, default the last slot)."""
+    B, Hq, Hkv, S, D = _check_decode_inputs(q, k_cache, v_cache)
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _require(t.dtype == k_cache.dtype and t.device == k_cache.device and t.is_contiguous()
+                 and t.numel() == B * Hkv * D, f"{name} must be a contiguous [B, Hkv, D] tensor like the cache")
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous(), "out must be like q")
+    if isinstance(pos, torch.Tensor):
+        pos_t = _as_int32(pos, B, k_cache.device)
+        mp = S - 1 if max_pos is None else int(max_pos)
+    else:
+        host = [int(v) for v in (pos if hasattr(pos, "__len__") else [pos] * B)]
+        _require(len(host) == B, "need one position per batch row")
+        if all(v == host[0] for v in host) and max_pos is None and 0 <= host[0] < S:
+            pos_t, mp = None, host[0]
+        else:
+            pos_t = _as_int32(host, B, k_cache.device)
+            mp = max(0, min(S - 1, max(host))) if max_pos is None else int(max_pos)
+    plan_len = min(mp + 1, S)
+    if num_splits > 0:
+        chunk = -(-plan_len // num_splits)
+        splits = -(-plan_len // chunk)
+    else:
+        splits = decode_num_splits(B, Hq, Hkv, plan_len)
+    need = decode_workspace_bytes(B, Hq, Hkv, D, splits) if splits > 1 else 0
+    ws = workspace if workspace is not None else _workspace(k_cache.device, need)
+    ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = _lib.ada_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(pos_t), B, Hq,
+                              Hkv, D, S, mp, ctypes.c_float(scale), _DTYPE_CODES[k_cache.dtype], _ptr(out), _ptr(ws),
+                              ws_bytes, ctypes.c_void_p(_stream(k_cache.device)), int(num_splits))
+    _check(rc, "ada_decode_step")
+    return out
+
+
 def decode_attn_gqa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len,
                     scale: float | None = None, out: torch.Tensor | None = None,
                     max_kv_len: int | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
@@ -345,7 +392,7 @@ def decode_attn_gqa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
 
 __all__ = [
     "AdaError", "F16", "BF16", "HEAD_DIM", "MAX_SPLITS", "EXPORTS", "LIB_PATH", "load_library",
-    "kv_append", "decode_attn_gqa", "decode_attn_gqa_ex", "decode_partial", "decode_combine", "decode_num_splits", "decode_workspace_bytes",
+    "kv_append", "decode_attn_gqa", "decode_attn_gqa_ex", "decode_partial", "decode_combine", "decode_step", "decode_num_splits", "decode_workspace_bytes",
     "new_workspace", "workspace_layout", "device_num_cus", "status_string", "last_hip_error",
     "abi_version",
 ]

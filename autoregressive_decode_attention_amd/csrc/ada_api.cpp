@@ -8,6 +8,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <climits>
 #include <cstdint>
 
 #include "ada_internal.h"
@@ -210,7 +211,9 @@ int prepare_decode(const void* q, const void* k_cache, const void* v_cache, cons
 
 int check_workspace(const void* workspace, size_t workspace_bytes, int batch, int n_head,
                     int n_kv_head, int splits) {
-  const size_t need = ada::workspace_layout(batch, n_head, n_kv_head, ada::kHeadDim, splits).total;
+  const ada::WorkspaceLayout w = ada::workspace_layout(batch, n_head, n_kv_head, ada::kHeadDim, splits);
+  if (w.total - w.acc_offset > static_cast<size_t>(INT32_MAX)) return ADA_ERR_SHAPE;  // 32-bit offsets
+  const size_t need = w.total;
   if (!workspace || workspace_bytes < need) return ADA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ADA_ERR_ALIGN;
   return ADA_OK;
@@ -253,6 +256,38 @@ int ada_decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache,
   return ada_decode_attn_gqa_ex(q, k_cache, v_cache, kv_len, batch, n_head, n_kv_head, head_dim,
                                 capacity, max_kv_len, scale, dtype, out, workspace,
                                 workspace_bytes, stream, 0);
+}
+
+int ada_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const int32_t* pos, int batch, int n_head, int n_kv_head, int head_dim,
+                    int capacity, int max_pos, float scale, int dtype, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream, int num_splits) {
+  if (max_pos < 0 || max_pos >= capacity) {
+    if (dtype != ADA_F16 && dtype != ADA_BF16) return ADA_ERR_DTYPE;
+    return ADA_ERR_SHAPE;
+  }
+  ada::DecodeLaunch p{};
+  int rc = prepare_decode(q, k_cache, v_cache, nullptr, batch, n_head, n_kv_head, head_dim, capacity,
+                          max_pos + 1, scale, dtype, num_splits, stream, &p);
+  if (rc != ADA_OK || batch == 0) return rc;
+  if (!k_new || !v_new || !out) return ADA_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(out)) return ADA_ERR_ALIGN;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.pos = pos;
+  p.out = out;
+  p.direct = p.splits == 1;
+  if (!p.direct) {
+    rc = check_workspace(workspace, workspace_bytes, batch, n_head, n_kv_head, p.splits);
+    if (rc != ADA_OK) return rc;
+    p.workspace = workspace;
+  }
+  hipError_t e = ada::launch_partial(p);
+  if (e != hipSuccess) return hip_fail(e);
+  if (p.direct) return ADA_OK;
+  ada::CombineLaunch c{workspace, out, batch, n_head, n_kv_head, p.splits, dtype, p.stream};
+  e = ada::launch_combine(c);
+  return e == hipSuccess ? ADA_OK : hip_fail(e);
 }
 
 int ada_decode_partial(const void* q, const void* k_cache, const void* v_cache,

@@ -35,6 +35,9 @@ struct DecodeLaunch {
   const void* k_cache;
   const void* v_cache;
   const int32_t* kv_len;
+  const void* k_new;    // decode step: new rows appended at pos (else NULL)
+  const void* v_new;
+  const int32_t* pos;   // decode step: device slots, or NULL (slot max_kv_len - 1)
   void* out;        // written when direct
   void* workspace;  // partials written when !direct
   int batch, n_head, n_kv_head, capacity, max_kv_len;

@@ -194,10 +194,18 @@ __device__ __forceinline__ float dot8(const uint4& k, const uint4& q, float s) {
 //   T  rows per lane group per tile
 //   P  tiles in flight ahead of the one being computed (register ring of
 //      P + 1 tiles; the ring is unrolled so buffers never move)
+//
+// With k_new != NULL the call is a whole decode step: the new key/value rows
+// (k_new, v_new: [B, H_kv, D]) belong at slot p = pos[b] (or max_kv_len - 1
+// when pos is NULL), the workgroup of split 0 writes them into the cache, the
+// workgroup whose range holds slot p reads that row from k_new/v_new instead
+// of the cache (no launch waits for the write), and the live prefix is
+// p + 1 slots. Otherwise lengths come from kv_len (or max_kv_len).
 template <class E, int G, int L, int T, int P>
 __global__ __launch_bounds__(kThreads) void partial_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ kv_len,
+    const uint16_t* __restrict__ q, uint16_t* k_cache, uint16_t* v_cache,
+    const int32_t* __restrict__ kv_len, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, const int32_t* __restrict__ pos,
     uint16_t* __restrict__ out, float2* __restrict__ part_ml, float* __restrict__ part_acc, int n_kv_head, int capacity, int max_kv_len, int chunk,
     int direct, float scale_log2) {
   constexpr int D = kHeadDim;
@@ -218,13 +226,31 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   const int grp = lane / L;   // row of this lane within a wave-wide load
   const int sub = lane % L;   // dims [8*sub, +8) (and [64 + 8*sub, +8) when L == 8)
 
+  const size_t head_off = (static_cast<size_t>(b) * n_kv_head + g) * static_cast<size_t>(capacity) * D;
+  const size_t new_row = (static_cast<size_t>(b) * n_kv_head + g) * D;  // row (b, g) of k_new / v_new
+  int p_new = -1;  // slot this call appends, if any
+  if (k_new != nullptr) {
+    p_new = pos != nullptr ? pos[b] : max_kv_len - 1;
+    if (split == 0 && tid < 32 && p_new >= 0 && p_new < capacity) {
+      const int c = 8 * (tid & 15);  // one 16-byte chunk of the key (tid < 16) or value row
+      const size_t dst = head_off + static_cast<size_t>(p_new) * D + c;
+      if (tid < 16) {
+        *reinterpret_cast<uint4*>(k_cache + dst) = load16(k_new + new_row + c);
+      } else {
+        *reinterpret_cast<uint4*>(v_cache + dst) = load16(v_new + new_row + c);
+      }
+    }
+  }
+
   // kv_len == NULL: every row holds max_kv_len live slots (one position for
   // the whole batch), and nothing is read before the K/V stream starts.
   int n = max_kv_len;
-  if (kv_len != nullptr) {
+  if (k_new != nullptr) {
+    n = p_new + 1;
+  } else if (kv_len != nullptr) {
     n = kv_len[b];
-    n = n < 0 ? 0 : (n > max_kv_len ? max_kv_len : n);
   }
+  n = n < 0 ? 0 : (n > max_kv_len ? max_kv_len : n);
   const int nsplit = (n + chunk - 1) / chunk;  // splits holding live slots
   const size_t out_row0 = (static_cast<size_t>(b) * n_head + static_cast<size_t>(g) * G) * D;
 
@@ -258,9 +284,10 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     for (int d = 0; d < DPL; ++d) acc[i][d] = 0.0f;
   }
 
-  const size_t head_off = (static_cast<size_t>(b) * n_kv_head + g) * static_cast<size_t>(capacity) * D;
   const uint16_t* kbase = k_cache + head_off + 8 * sub;
   const uint16_t* vbase = v_cache + head_off + 8 * sub;
+  const uint16_t* knew = k_new != nullptr ? k_new + new_row + 8 * sub : kbase;
+  const uint16_t* vnew = v_new != nullptr ? v_new + new_row + 8 * sub : vbase;
 
   const int wave_first = row_begin + wave * kWaveRows;
   const int span = row_end - wave_first;
@@ -272,14 +299,24 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   // bounds and finite) and given zero weight, so no branch guards the loads.
   uint4 kb[NB][T][CH], vb[NB][T][CH];
   auto load_tile = [&](int base, uint4 (&kr)[T][CH], uint4 (&vr)[T][CH]) {
+    // Only the tile holding the appended slot (the last live row) reads a row
+    // from k_new / v_new; the test is uniform across the wave.
+    const int tile_row0 = base - grp;
+    const bool has_new = p_new >= tile_row0 && p_new < tile_row0 + kWaveRows;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       const int r = min(base + t * kRows, last_row);
       const size_t off = static_cast<size_t>(r) * D;
+      const uint16_t* kp = kbase + off;
+      const uint16_t* vp = vbase + off;
+      if (has_new && r == p_new) {
+        kp = knew;
+        vp = vnew;
+      }
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
-        kr[t][c] = load16_stream(kbase + off + 64 * c);
-        vr[t][c] = load16_stream(vbase + off + 64 * c);
+        kr[t][c] = load16_stream(kp + 64 * c);
+        vr[t][c] = load16_stream(vp + 64 * c);
       }
     }
   };
@@ -412,32 +449,45 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   }
 }
 
+// Buffer resource over a workspace array: 32-bit byte offsets instead of
+// 64-bit addresses keep one register per in-flight load. Word 3 is the gfx9
+// raw-buffer format (32-bit data format); the host keeps every offset below
+// 2^31.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t workspace_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), 0x7fffffff,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ float2 buffer_load_f2(__amdgpu_buffer_rsrc_t r, uint32_t byte_offset) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_offset, 0, 0));
+}
+
 // Combine kernel: one workgroup per (KV head, batch row), one wavefront per
 // query head of the group, two dims per lane. It merges the num_splits
 // partials of its head in split order with log-sum-exp weights,
 //   M = max_s m_s,  out = sum_s exp2(m_s - M) acc_s / sum_s exp2(m_s - M) l_s,
 // then rounds to the output type. Empty splits carry m = -inf and weigh 0
-// (their accumulators are never read); a head whose splits are all empty
+// (their accumulators are never used); a head whose splits are all empty
 // (kv_len 0) gets zeros.
 //
 // Splits are taken in batches of kBatch whose loads are all issued before
 // any is used, and batches are merged online (running max, rescaled sums),
-// so a call waits for memory about once per batch and needs no LDS or
-// barrier.
+// so a call waits for memory once per batch and needs no LDS or barrier.
 template <class E>
 __global__ __launch_bounds__(64 * kMaxGroup) void combine_kernel(
     uint16_t* __restrict__ out, const float2* __restrict__ part_ml,
     const float* __restrict__ part_acc, int n_kv_head, int group, int num_splits) {
   constexpr int D = kHeadDim;
-  constexpr int kBatch = 16;
+  constexpr int kBatch = 32;  // the heuristic rarely asks for more: one memory wait
   const int g = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int i = threadIdx.x >> 6;  // query head within the group
   const int n_head = n_kv_head * group;
-  const size_t head_row = static_cast<size_t>(b) * n_head + static_cast<size_t>(g) * group + i;
-  const size_t split_stride = static_cast<size_t>(gridDim.y) * n_head;  // split-major partials
-  const float2* acc2 = reinterpret_cast<const float2*>(part_acc);
+  const uint32_t head_row = static_cast<uint32_t>(b) * n_head + static_cast<uint32_t>(g) * group + i;
+  const uint32_t split_stride = static_cast<uint32_t>(gridDim.y) * n_head;  // split-major partials
+  const __amdgpu_buffer_rsrc_t ml_r = workspace_rsrc(part_ml);
+  const __amdgpu_buffer_rsrc_t acc_r = workspace_rsrc(part_acc);
 
   float m_run = kNegInf, l_run = 0.0f;
   float2 o = make_float2(0.0f, 0.0f);
@@ -447,9 +497,9 @@ __global__ __launch_bounds__(64 * kMaxGroup) void combine_kernel(
     for (int k = 0; k < kBatch; ++k) {
       const int s = s0 + k;
       if (s < num_splits) {
-        const size_t row = head_row + static_cast<size_t>(s) * split_stride;
-        ml[k] = part_ml[row];
-        a[k] = acc2[row * (D / 2) + lane];
+        const uint32_t row = head_row + static_cast<uint32_t>(s) * split_stride;
+        ml[k] = buffer_load_f2(ml_r, row * 8u);
+        a[k] = buffer_load_f2(acc_r, row * (D * 4u) + lane * 8u);
       } else {
         ml[k] = make_float2(kNegInf, 0.0f);
         a[k] = make_float2(0.0f, 0.0f);
@@ -477,7 +527,7 @@ __global__ __launch_bounds__(64 * kMaxGroup) void combine_kernel(
   const float inv = l_run > 0.0f ? 1.0f / l_run : 0.0f;
   const uint32_t packed = static_cast<uint32_t>(E::round(o.x * inv)) |
                           (static_cast<uint32_t>(E::round(o.y * inv)) << 16);
-  reinterpret_cast<uint32_t*>(out + head_row * D)[lane] = packed;
+  reinterpret_cast<uint32_t*>(out + static_cast<size_t>(head_row) * D)[lane] = packed;
 }
 
 // In-place append: row pos[b] of every KV head of batch row b, K and V, as
@@ -528,8 +578,10 @@ hipError_t launch_partial_g(const DecodeLaunch& p) {
   }
   hipLaunchKernelGGL((partial_kernel<E, G, C::L, C::T, C::P>), dim3(p.splits, p.n_kv_head, p.batch),
                      dim3(kThreads), 0, p.stream, static_cast<const uint16_t*>(p.q),
-                     static_cast<const uint16_t*>(p.k_cache), static_cast<const uint16_t*>(p.v_cache),
-                     p.kv_len, static_cast<uint16_t*>(p.out), part_ml, part_acc, p.n_kv_head,
+                     static_cast<uint16_t*>(const_cast<void*>(p.k_cache)),
+                     static_cast<uint16_t*>(const_cast<void*>(p.v_cache)), p.kv_len,
+                     static_cast<const uint16_t*>(p.k_new), static_cast<const uint16_t*>(p.v_new), p.pos,
+                     static_cast<uint16_t*>(p.out), part_ml, part_acc, p.n_kv_head,
                      p.capacity, p.max_kv_len, p.chunk, p.direct ? 1 : 0, p.scale_log2);
   return hipGetLastError();
 }

@@ -76,9 +76,10 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(KERNEL_SOURCE.read_bytes()).hexdigest()[:16]
 
 
-def pmc_traffic(bytes_key: str = "mha_sweep") -> float | None:
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary,
-    or None when there is none or the kernel source changed since it was taken."""
+def pmc_traffic() -> float | None:
+    """HBM bytes of one step's partial-kernel launches from the committed
+    rocprofv3 counter summary, or None when there is none or the kernel source
+    changed since the counters were taken."""
     if not PMC_SUMMARY.exists():
         return None
     text = PMC_SUMMARY.read_text()
@@ -124,20 +125,21 @@ class Sweep:
         self.ws = ada.new_workspace(ws_need, device)
 
     def step(self, set_index: int | None = None):
-        """Append then decode (partial + combine kernels) at each kv_len, on the
-        next cache set (or ``set_index``). Lengths are one host-side position per
-        call (batch 1), so the kernels read no length from the device."""
+        """One decode step at each kv_len -- append the new row at slot kv_len - 1
+        and attend over kv_len slots, as one ada_decode_step call (partial
+        kernel with the append folded in, then the combine kernel) -- on the
+        next cache set (or ``set_index``). The position is a host int (batch
+        1), so the kernels read no length from the device."""
         ada = self.ada
         row = self.caches[(self.i if set_index is None else set_index) % self.sets]
         self.i += 1
         for j, n in enumerate(SWEEP):
             k, v = row[j]
-            ada.kv_append(self.k_new, self.v_new, k, v, self.pos[j])
-            _, used = ada.decode_partial(self.q[j], k, v, None, scale=self.scale, max_kv_len=n, workspace=self.ws)
-            ada.decode_combine(self.ws, used, self.out[j], self.shape.n_kv_head)
+            ada.decode_step(self.q[j], self.k_new, self.v_new, k, v, n - 1, scale=self.scale, out=self.out[j],
+                            workspace=self.ws)
 
     def capture(self):
-        """One HIP graph per cache set holding a whole step (9 kernels)."""
+        """One HIP graph per cache set holding a whole step (6 kernels)."""
         self.graphs = []
         stream = torch.cuda.Stream()
         stream.wait_stream(torch.cuda.current_stream())
@@ -241,6 +243,65 @@ def time_long_context(ada, device, iters: int = 20) -> dict:
             "call_frac_of_peak": round(nbytes / whole / 1e3 / PEAK_HBM_GBS, 4)}
 
 
+def time_s2pro_run(ada, device) -> dict:
+    """The S2-Pro-shaped run (36 layers, 32/8 heads, fp16, capacity 32768,
+    prefill 234, then 1024 decode steps): one HIP graph holds a whole decode
+    step -- per layer one ada_decode_step (append at slot 234 + i and attend
+    over 235 + i slots) -- plus a device-side increment of the position, so
+    one replay per step runs the whole run with no host work in between.
+    Timed over all 1024 replays (36 864 decode calls)."""
+    wl = W.WORKLOADS["s2pro_run"]
+    shp = wl.shape
+    L, T0, N = wl.layers, wl.prefill, wl.steps
+    B, Hq, Hkv, D, S = shp.batch, shp.n_head, shp.n_kv_head, shp.head_dim, shp.capacity
+    last = T0 + N
+    dt = W.TORCH_DTYPES[shp.dtype]
+    kc = torch.zeros((L, B, Hkv, S, D), dtype=dt, device=device)
+    vc = torch.zeros_like(kc)
+    for layer in range(L):
+        x = W.decode_inputs(W.DecodeShape(B, Hq, Hkv, D, T0, shp.dtype), [T0], W.seed_for(2, layer),
+                            device=device, tail="random")
+        kc[layer, :, :, :T0] = x["k_cache"]
+        vc[layer, :, :, :T0] = x["v_cache"]
+    k_new = W.randn16((L, B, Hkv, D), shp.dtype, W.seed_for(2, 20_000), device=device)
+    v_new = W.randn16((L, B, Hkv, D), shp.dtype, W.seed_for(2, 20_001), device=device)
+    q = W.randn16((L, B, Hq, D), shp.dtype, W.seed_for(2, 20_002), device=device)
+    out = torch.empty((L, B, Hq, D), dtype=dt, device=device)
+    pos = torch.full((B,), T0, dtype=torch.int32, device=device)
+    splits = ada.decode_num_splits(B, Hq, Hkv, last)
+    ws = ada.new_workspace(ada.decode_workspace_bytes(B, Hq, Hkv, D, max(2, splits)), device)
+    scale = 1.0 / math.sqrt(D)
+
+    def step():
+        for layer in range(L):
+            ada.decode_step(q[layer], k_new[layer], v_new[layer], kc[layer], vc[layer], pos, scale=scale,
+                            out=out[layer], max_pos=last - 1, workspace=ws)
+        pos.add_(1)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm the binding outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    pos.fill_(T0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(N):
+        g.replay()
+    torch.cuda.synchronize()
+    run_ms = (time.perf_counter() - t0) * 1e3
+    nbytes = L * sum(decode_bytes(B, Hq, Hkv, D, [n]) for n in range(T0 + 1, last + 1))
+    del kc, vc
+    return {"workload": "s2pro_run: 36 layers, 32/8 heads, head_dim 128, fp16, capacity 32768, prefill 234, "
+                        "1024 steps (kv_len 235..1258), one decode step (append + attend) per layer, one graph replay per step",
+            "run_ms": round(run_ms, 2), "ms_per_step": round(run_ms / N, 4),
+            "us_per_layer_call": round(run_ms * 1e3 / (N * L), 2), "run_bytes": nbytes,
+            "GBs": round(nbytes / (run_ms * 1e-3) / 1e9, 1), "splits": splits}
+
+
 def cpu_baseline(seconds: float) -> dict:
     """The fp64 oracle on the same step (three decode calls of the sweep), run
     until ``seconds`` of CPU time have passed (at least one step)."""
@@ -339,6 +400,7 @@ def main(argv=None):
             "eager_GBs": round(sweep.step_bytes / (eager_ms * 1e-3) / 1e9, 1)}
     if not args.no_long_context:
         also["long_context"] = time_long_context(ada, device)
+        also["s2pro_run"] = time_s2pro_run(ada, device)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -347,9 +409,12 @@ def main(argv=None):
         "config": {"workload": "mha_sweep: one-token decode, batch 1, 16 heads = 16 KV heads, head_dim 128, fp16, "
                                "kv_len 1024/4096/8192 (append + decode each), capacity 8192, "
                                f"cold caches rotated over {sweep.sets} sets",
-                   "step_bytes": sweep.step_bytes, "kernels_per_step": 9, "launch": launch},
+                   "step_bytes": sweep.step_bytes, "kernels_per_step": 6, "launch": launch},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "traffic_basis": "HBM bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated) of the three partial "
+                                      "launches of one step; algorithmic bytes of the same launches: "
+                                      f"{sum(sweep.decode_bytes)}",
                      "kernel": "partial_kernel (split-KV partial of the decode; the combine kernel follows it)",
                      "bytes_per_launch": sweep.decode_bytes,
                      "us_per_launch": [round(u, 2) for u in part_us]},

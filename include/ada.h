@@ -183,6 +183,33 @@ int ada_decode_attn_gqa_ex(const void* q, const void* k_cache, const void* v_cac
                            int num_splits);
 
 /*
+ * One whole decode step in one call: append the new key/value rows, then
+ * attend over the prefix that ends with them ([FORWARD-STEP] section 4: the
+ * cache write at position_id followed by attention over slots
+ * 0..position_id). Equivalent to ada_kv_append(k_new, v_new, k_cache, v_cache,
+ * pos) followed by ada_decode_attn_gqa with kv_len[b] = pos[b] + 1, with
+ * one kernel launch fewer: the kernel that attends reads the new rows from
+ * k_new/v_new while another workgroup of the same launch writes them into
+ * the cache.
+ *
+ *   k_new, v_new  device, [batch, n_kv_head, head_dim].
+ *   k_cache,      device, [batch, n_kv_head, capacity, head_dim], updated in
+ *   v_cache       place at slot pos[b] (when 0 <= pos[b] < capacity).
+ *   pos           device int32 [batch], or NULL: every row at slot max_pos.
+ *   max_pos       host upper bound on pos[b], 0 <= max_pos < capacity (else
+ *                 ADA_ERR_SHAPE); sizes the launch. A row attends over
+ *                 min(pos[b], max_pos) + 1 slots; pos[b] < 0 gives a zero row
+ *                 and writes nothing.
+ *   num_splits    0 = heuristic, else forced as in ada_decode_attn_gqa_ex.
+ * Other arguments as ada_decode_attn_gqa_ex. k_new/v_new must not overlap
+ * the caches or out.
+ */
+int ada_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const int32_t* pos, int batch, int n_head, int n_kv_head, int head_dim,
+                    int capacity, int max_pos, float scale, int dtype, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream, int num_splits);
+
+/*
  * The two halves of a decode call, for callers that merge partial results
  * themselves -- e.g. key ranges held by different devices, whose partials are
  * concatenated along the split axis and combined once.

@@ -151,6 +151,24 @@ def test_partial_and_combine_validation(ada):
     assert comb(NUL, 0, 0, 32, 8, 128, 4, 0, NUL, NUL) == 0
 
 
+def test_decode_step_validation(ada):
+    f = ada._lib.ada_decode_step
+    args = lambda **kw: [kw.get("q", P), kw.get("kn", P2), kw.get("vn", P3), P4, P5, NUL, 1, 32, 8,
+                         kw.get("D", 128), 2048, kw.get("mp", 399), ctypes.c_float(0.08), kw.get("dtype", 0),
+                         kw.get("out", P), kw.get("ws", NUL), kw.get("ws_bytes", 0), NUL, kw.get("splits", 2)]
+    assert f(*args(mp=2048)) == -2
+    assert f(*args(mp=-1)) == -2
+    assert f(*args(dtype=9)) == -4
+    assert f(*args(kn=NUL)) == -1
+    assert f(*args(vn=NUL)) == -1
+    assert f(*args(out=NUL)) == -1
+    assert f(*args(q=NUL)) == -1
+    assert f(*args(kn=MIS)) == -9
+    assert f(*args(D=64)) == -5
+    assert f(*args()) == -7                     # two splits need a workspace
+    assert f(*args(splits=300)) == -8
+
+
 def test_workspace_bytes_arithmetic(ada):
     r256 = lambda x: (x + 255) // 256 * 256
     for B, Hq, Hkv, splits in ((1, 32, 8, 4), (8, 32, 8, 8), (4, 32, 8, 33), (1, 16, 16, 32), (3, 6, 3, 7)):

@@ -432,3 +432,48 @@ def test_lockstep_lengths_from_the_host(ada, ora):
     x = gpu(W.decode_inputs(shp, [0] * 4, 719, tail="nan"))
     out = ada.decode_attn_gqa(x["q"], x["k_cache"], x["v_cache"], 0, scale=SCALE)
     assert torch.count_nonzero(out) == 0
+
+
+# ---------------------------------------------------------------------------
+# The whole step in one call.
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_decode_step_equals_append_then_decode(ada, ora, dtype):
+    """ada_decode_step = ada_kv_append + ada_decode_attn_gqa with kv_len = pos + 1,
+    bit for bit, for lockstep and per-row positions ([FORWARD-STEP] section 4)."""
+    B, Hq, Hkv, D, S = 4, 32, 8, 128, 3000
+    for k, (pos, splits) in enumerate((([2999] * 4, 0), ([1234] * 4, 7), ([0, 5, 2999, 1500], 0),
+                                        ([-1, 3000, 77, 2000], 3), ([0] * 4, 1))):
+        say(f"case decode step {dtype} pos={pos} splits={splits}")
+        # finite slots: those before the new row; a position past the cache leaves it whole
+        lens = [S if p >= S else max(0, p) for p in pos]
+        x = W.decode_inputs(W.DecodeShape(B, Hq, Hkv, D, S, dtype), lens, 720 + k, tail="nan")
+        kn, vn = W.append_inputs(B, Hkv, D, dtype, 740 + k)
+        d1, d2 = gpu(x), gpu(x)
+        kn_d, vn_d = kn.cuda(), vn.cuda()
+        pos_t = torch.tensor(pos, dtype=torch.int32, device="cuda")
+        mp = max(0, min(S - 1, max(pos)))
+        fused = ada.decode_step(d1["q"], kn_d, vn_d, d1["k_cache"], d1["v_cache"], pos, scale=SCALE,
+                                num_splits=splits)
+        ada.kv_append(kn_d, vn_d, d2["k_cache"], d2["v_cache"], pos_t)
+        lens_t = torch.tensor([p + 1 if p >= 0 else 0 for p in pos], dtype=torch.int32, device="cuda")
+        ref = ada.decode_attn_gqa_ex(d2["q"], d2["k_cache"], d2["v_cache"], lens_t, scale=SCALE,
+                                     max_kv_len=mp + 1, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(d1["k_cache"].view(torch.int16), d2["k_cache"].view(torch.int16))
+        assert torch.equal(d1["v_cache"].view(torch.int16), d2["v_cache"].view(torch.int16))
+        assert torch.equal(fused, ref), "decode_step differs from append + decode"
+        kc, vc = ora.kv_append(kn, vn, x["k_cache"], x["v_cache"], pos)
+        to16 = lambda a: torch.from_numpy(a.view(np.int16)).view(W.TORCH_DTYPES[dtype])
+        eff = [min(p, mp) + 1 if p >= 0 else 0 for p in pos]
+        want = ora.decode(x["q"], to16(kc), to16(vc), eff, SCALE)
+        assert_parity(fused, want, dtype, f"decode step pos={pos}")
+
+
+def test_decode_step_position_zero_returns_new_value(ada):
+    """Position 0: the only slot is the new one, so out = v_new exactly."""
+    x = gpu(W.decode_inputs(shape(2, 16, 4, 64, "bf16"), [0, 0], 760, tail="nan"))
+    kn, vn = W.append_inputs(2, 4, 128, "bf16", 761)
+    out = ada.decode_step(x["q"], kn.cuda(), vn.cuda(), x["k_cache"], x["v_cache"], 0, scale=SCALE)
+    assert torch.equal(out, vn.cuda().repeat_interleave(4, dim=1))
