@@ -302,6 +302,48 @@ def time_s2pro_run(ada, device) -> dict:
             "GBs": round(nbytes / (run_ms * 1e-3) / 1e9, 1), "splits": splits}
 
 
+def time_full_vs_active(ada, device, iters: int = 20) -> dict:
+    """The pages' experiment restated on this kernel (fish-speech #1310,
+    "CUDA benchmark"; VoxCPM #395, section 6.3): a decode call that attends
+    over the whole preallocated capacity (what a full-width mask costs: every
+    slot is read) against one over the live prefix only, at the S2-Pro shape
+    (capacity 32768, live 235 and 1258) and the MiniCPM shape (batch 4,
+    capacity 8192, live 1522 and 5617, two of that page's sampled positions).
+    Caches rotate so every call reads HBM."""
+    cases = [("s2pro", W.WORKLOADS["s2pro_run"].shape, (235, 1258)),
+             ("minicpm", W.WORKLOADS["minicpm_stream"].shape, (1522, 5617))]
+    res = {}
+    for name, shp, lives in cases:
+        B, Hq, Hkv, D, S = shp.batch, shp.n_head, shp.n_kv_head, shp.head_dim, shp.capacity
+        per_full = kv_bytes(Hkv, D, B * S)
+        R = max(2, math.ceil(2 * MALL_BYTES / per_full))
+        xs = [W.decode_inputs(shp, [S] * B, W.seed_for(2, 30_000 + r), device=device, tail="random") for r in range(R)]
+        ws = ada.new_workspace(ada.decode_workspace_bytes(B, Hq, Hkv, D, 256), device)
+        out = torch.empty_like(xs[0]["q"])
+
+        def timed(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            torch.cuda._sleep(SPIN_CYCLES)
+            a.record()
+            for i in range(iters):
+                x = xs[i % R]
+                ada.decode_attn_gqa(x["q"], x["k_cache"], x["v_cache"], None, max_kv_len=n, out=out, workspace=ws)
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / iters
+
+        full = timed(S)
+        row = {"capacity": S, "full_capacity_us": round(full, 2)}
+        for n in lives:
+            us = timed(n)
+            row[f"live_{n}_us"] = round(us, 2)
+            row[f"speedup_at_{n}"] = round(full / us, 2)
+        res[name] = row
+        del xs
+    return res
+
+
 def cpu_baseline(seconds: float) -> dict:
     """The fp64 oracle on the same step (three decode calls of the sweep), run
     until ``seconds`` of CPU time have passed (at least one step)."""
@@ -401,6 +443,7 @@ def main(argv=None):
     if not args.no_long_context:
         also["long_context"] = time_long_context(ada, device)
         also["s2pro_run"] = time_s2pro_run(ada, device)
+        also["full_capacity_vs_active_prefix"] = time_full_vs_active(ada, device)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

@@ -477,3 +477,62 @@ def test_decode_step_position_zero_returns_new_value(ada):
     kn, vn = W.append_inputs(2, 4, 128, "bf16", 761)
     out = ada.decode_step(x["q"], kn.cuda(), vn.cuda(), x["k_cache"], x["v_cache"], 0, scale=SCALE)
     assert torch.equal(out, vn.cuda().repeat_interleave(4, dim=1))
+
+
+def test_graph_replayed_steps_match_eager(ada, ora):
+    """A captured multi-layer decode step with a device-side position increment,
+    replayed several times with eager work and synchronisations in between:
+    every replay equals the same steps run eagerly, bit for bit, and the first
+    matches the oracle."""
+    L, B, Hq, Hkv, D, S, T0 = 3, 2, 32, 8, 128, 1024, 300
+    dt = torch.float16
+    xs = [W.decode_inputs(W.DecodeShape(B, Hq, Hkv, D, S, "fp16"), [T0] * B, 770 + l, tail="nan") for l in range(L)]
+    new = [W.append_inputs(B, Hkv, D, "fp16", 780 + l) for l in range(L)]
+    kg = torch.stack([x["k_cache"] for x in xs]).cuda()
+    vg = torch.stack([x["v_cache"] for x in xs]).cuda()
+    ke, ve = kg.clone(), vg.clone()
+    qg = torch.stack([x["q"] for x in xs]).cuda()
+    kn = torch.stack([n[0] for n in new]).cuda()
+    vn = torch.stack([n[1] for n in new]).cuda()
+    out_g = torch.empty((L, B, Hq, D), dtype=dt, device="cuda")
+    out_e = torch.empty_like(out_g)
+    pos = torch.full((B,), T0, dtype=torch.int32, device="cuda")
+    ws = ada.new_workspace(ada.decode_workspace_bytes(B, Hq, Hkv, D, 64), torch.device("cuda"))
+
+    def step(kc, vc, out, p, max_pos):
+        for l in range(L):
+            ada.decode_step(qg[l], kn[l], vn[l], kc[l], vc[l], p, scale=SCALE, out=out[l], max_pos=max_pos,
+                            workspace=ws)
+
+    def graph_step():
+        step(kg, vg, out_g, pos, S - 1)
+        pos.add_(1)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        graph_step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    kg.copy_(ke)
+    vg.copy_(ve)
+    pos.fill_(T0)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graph_step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (qg.float() * 2).sum()  # unrelated eager work between replays
+        pos_e = torch.full((B,), T0 + r, dtype=torch.int32, device="cuda")
+        step(ke, ve, out_e, pos_e, S - 1)
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, out_e), f"replay {r} differs from the eager step"
+        assert torch.equal(kg.view(torch.int16), ke.view(torch.int16)), f"replay {r}: key caches differ"
+        if r == 0:
+            for l in range(L):
+                kc, vc = ora.kv_append(new[l][0], new[l][1], xs[l]["k_cache"], xs[l]["v_cache"], [T0] * B)
+                to16 = lambda a: torch.from_numpy(a.view(np.int16)).view(dt)
+                want = ora.decode(xs[l]["q"], to16(kc), to16(vc), [T0 + 1] * B, SCALE)
+                assert_parity(out_g[l], want, "fp16", f"graph layer {l}")
