@@ -186,28 +186,185 @@ __device__ __forceinline__ float dot8(const uint4& k, const uint4& q, float s) {
 }
 
 // ---------------------------------------------------------------------------
-// Decode kernel.
+// Partial kernels: shared prologue and epilogue.
+
+// Where one workgroup stands: its split's live slot range and the indices of
+// its outputs. With k_new != NULL the call is a whole decode step: the new
+// key/value rows (k_new, v_new: [B, H_kv, D]) belong at slot p = pos[b] (or
+// max_kv_len - 1 when pos is NULL), the workgroup of split 0 writes them
+// into the cache, the workgroup whose range holds slot p reads that row from
+// k_new/v_new instead of the cache (no launch waits for the write), and the
+// live prefix is p + 1 slots. Otherwise lengths come from kv_len, or are
+// max_kv_len for every row when kv_len is NULL (one position for the whole
+// batch: nothing is read before the K/V stream starts).
+struct SplitRange {
+  int n;          // live slots of this batch row
+  int row_begin;  // this split's first slot
+  int last_row;   // this split's last live slot
+  int p_new;      // slot appended by this call, or -1
+  size_t head_off;   // (b, g) head of the caches, in elements
+  size_t new_row;    // (b, g) row of k_new / v_new, in elements
+  size_t out_row0;   // first output element of the group's query heads
+  size_t part_row0;  // first partial entry of the group's query heads
+};
+
+// Returns false when the split holds no live slot; it has then written what
+// an empty split owes (a zero row when writing the output directly, an
+// "empty" mark for the combine otherwise).
+template <int G>
+__device__ __forceinline__ bool begin_split(SplitRange& r, uint16_t* k_cache, uint16_t* v_cache,
+                                            const int32_t* kv_len, const uint16_t* k_new,
+                                            const uint16_t* v_new, const int32_t* pos, uint16_t* out,
+                                            float2* part_ml, int n_kv_head, int capacity,
+                                            int max_kv_len, int chunk, int direct) {
+  constexpr int D = kHeadDim;
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int n_head = n_kv_head * G;
+  r.head_off = (static_cast<size_t>(b) * n_kv_head + g) * static_cast<size_t>(capacity) * D;
+  r.new_row = (static_cast<size_t>(b) * n_kv_head + g) * D;
+  r.p_new = -1;
+  if (k_new != nullptr) {
+    r.p_new = pos != nullptr ? pos[b] : max_kv_len - 1;
+    if (split == 0 && tid < 32 && r.p_new >= 0 && r.p_new < capacity) {
+      const int c = 8 * (tid & 15);  // one 16-byte chunk of the key (tid < 16) or value row
+      const size_t dst = r.head_off + static_cast<size_t>(r.p_new) * D + c;
+      if (tid < 16) {
+        *reinterpret_cast<uint4*>(k_cache + dst) = load16(k_new + r.new_row + c);
+      } else {
+        *reinterpret_cast<uint4*>(v_cache + dst) = load16(v_new + r.new_row + c);
+      }
+    }
+  }
+  int n = max_kv_len;
+  if (k_new != nullptr) {
+    n = r.p_new + 1;
+  } else if (kv_len != nullptr) {
+    n = kv_len[b];
+  }
+  r.n = n < 0 ? 0 : (n > max_kv_len ? max_kv_len : n);
+  const int nsplit = (r.n + chunk - 1) / chunk;  // splits holding live slots
+  const size_t head_row0 = static_cast<size_t>(b) * n_head + static_cast<size_t>(g) * G;
+  r.out_row0 = head_row0 * D;
+  r.part_row0 = static_cast<size_t>(split) * gridDim.z * n_head + head_row0;  // split-major partials
+  if (split >= nsplit) {
+    if (direct) {
+      for (int idx = tid; idx < G * D; idx += kThreads) out[r.out_row0 + idx] = 0;
+    } else if (tid < G) {
+      part_ml[r.part_row0 + tid] = make_float2(kNegInf, 0.0f);
+    }
+    return false;
+  }
+  r.row_begin = split * chunk;
+  r.last_row = min(r.row_begin + chunk, r.n) - 1;
+  return true;
+}
+
+// Sum V per-lane values over the 64 / L lane groups of a wavefront (lanes
+// equal modulo L), two values per exchange: a lane swap of registers a and b
+// followed by an add leaves a's pair sum in the lanes whose exchange bit is
+// clear and b's in the others, so each step halves the live registers. At
+// the end lane l holds, in x[0 .. V / (64 / L)), the sums of values
+// u + (V / (64 / L)) * (l / L).
+template <int L, int V>
+__device__ __forceinline__ void sum_lane_groups(float (&x)[V], int lane) {
+  constexpr int NG = 64 / L;
+  static_assert(V % NG == 0, "values must split evenly over the lane groups");
+#pragma unroll
+  for (int r = 0; r < V / 2; ++r) {  // lanes 32 apart
+    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[r]), __float_as_uint(x[r + V / 2]), false, false);
+    x[r] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  }
+#pragma unroll
+  for (int r = 0; r < V / 4; ++r) {  // lanes 16 apart
+    auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[r]), __float_as_uint(x[r + V / 4]), false, false);
+    x[r] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  }
+  if constexpr (L == 8) {  // lanes 8 apart, within a 16-lane row
+    const bool hi = (lane & 8) != 0;
+#pragma unroll
+    for (int r = 0; r < V / 8; ++r) {
+      const float mine = hi ? x[r + V / 8] : x[r];
+      const float send = hi ? x[r] : x[r + V / 8];
+      x[r] = mine + dpp<kDppRor8>(send);
+    }
+  }
+}
+
+// Merge the 4 wavefronts' states through LDS and write either the output
+// (one split) or this split's partial. Each wave passes its state: m[i] and
+// l[i] (the same in every lane) and the accumulator sums as left by
+// sum_lane_groups over acc[G][128 / L] flattened head-major, where lane
+// group g's sub-lane s held dims [8*s + 64*c, +8) in slots 8*c .. 8*c + 7.
+template <class E, int G, int L>
+__device__ __forceinline__ void finish_split(const SplitRange& r, const float (&m)[G], const float (&l)[G],
+                                             const float (&red)[G * (128 / L)], uint16_t* out,
+                                             float2* part_ml, float* part_acc, int direct) {
+  constexpr int D = kHeadDim;
+  constexpr int DPL = 128 / L;
+  constexpr int V = G * DPL;
+  constexpr int PER = V / (64 / L);  // sums held per lane
+  __shared__ float s_acc[kWaves][G][D];
+  __shared__ float2 s_ml[kWaves][G];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int sub = lane % L;
+  const int v0 = PER * (lane / L);
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int v = v0 + u;
+    const int i = v / DPL;
+    const int slot = v % DPL;
+    s_acc[wave][i][8 * sub + 64 * (slot / 8) + slot % 8] = red[u];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) s_ml[wave][i] = make_float2(m[i], l[i]);
+  }
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int i = idx / D;
+    const int d = idx % D;
+    float mw = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mw = fmaxf(mw, s_ml[w][i].x);
+    const float ref = finite_ref(mw);
+    float lsum = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = fast_exp2(s_ml[w][i].x - ref);
+      lsum += s_ml[w][i].y * wt;
+      o += s_acc[w][i][d] * wt;
+    }
+    if (direct) {
+      out[r.out_row0 + idx] = E::round(o / lsum);
+    } else {
+      const size_t pr = r.part_row0 + i;
+      part_acc[pr * D + d] = o;
+      if (d == 0) part_ml[pr] = make_float2(mw, lsum);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Partial kernel.
 //
 // Template parameters:
-//   G  query heads per KV head (1..8)
+//   G  query heads per KV head
 //   L  lanes per key row (8: 16 dims per lane; 16: 8 dims per lane)
 //   T  rows per lane group per tile
 //   P  tiles in flight ahead of the one being computed (register ring of
 //      P + 1 tiles; the ring is unrolled so buffers never move)
-//
-// With k_new != NULL the call is a whole decode step: the new key/value rows
-// (k_new, v_new: [B, H_kv, D]) belong at slot p = pos[b] (or max_kv_len - 1
-// when pos is NULL), the workgroup of split 0 writes them into the cache, the
-// workgroup whose range holds slot p reads that row from k_new/v_new instead
-// of the cache (no launch waits for the write), and the live prefix is
-// p + 1 slots. Otherwise lengths come from kv_len (or max_kv_len).
 template <class E, int G, int L, int T, int P>
 __global__ __launch_bounds__(kThreads) void partial_kernel(
     const uint16_t* __restrict__ q, uint16_t* k_cache, uint16_t* v_cache,
     const int32_t* __restrict__ kv_len, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, const int32_t* __restrict__ pos,
-    uint16_t* __restrict__ out, float2* __restrict__ part_ml, float* __restrict__ part_acc, int n_kv_head, int capacity, int max_kv_len, int chunk,
-    int direct, float scale_log2) {
+    uint16_t* __restrict__ out, float2* __restrict__ part_ml, float* __restrict__ part_acc,
+    int n_kv_head, int capacity, int max_kv_len, int chunk, int direct, float scale_log2) {
   constexpr int D = kHeadDim;
   constexpr int CH = 16 / L;             // 16-byte chunks per lane per row
   constexpr int DPL = 8 * CH;            // dims per lane
@@ -216,63 +373,24 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   constexpr int kTile = kWaveRows * kWaves;
   constexpr int NB = P + 1;
 
-  const int split = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  const int n_head = n_kv_head * G;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int grp = lane / L;   // row of this lane within a wave-wide load
   const int sub = lane % L;   // dims [8*sub, +8) (and [64 + 8*sub, +8) when L == 8)
 
-  const size_t head_off = (static_cast<size_t>(b) * n_kv_head + g) * static_cast<size_t>(capacity) * D;
-  const size_t new_row = (static_cast<size_t>(b) * n_kv_head + g) * D;  // row (b, g) of k_new / v_new
-  int p_new = -1;  // slot this call appends, if any
-  if (k_new != nullptr) {
-    p_new = pos != nullptr ? pos[b] : max_kv_len - 1;
-    if (split == 0 && tid < 32 && p_new >= 0 && p_new < capacity) {
-      const int c = 8 * (tid & 15);  // one 16-byte chunk of the key (tid < 16) or value row
-      const size_t dst = head_off + static_cast<size_t>(p_new) * D + c;
-      if (tid < 16) {
-        *reinterpret_cast<uint4*>(k_cache + dst) = load16(k_new + new_row + c);
-      } else {
-        *reinterpret_cast<uint4*>(v_cache + dst) = load16(v_new + new_row + c);
-      }
-    }
-  }
-
-  // kv_len == NULL: every row holds max_kv_len live slots (one position for
-  // the whole batch), and nothing is read before the K/V stream starts.
-  int n = max_kv_len;
-  if (k_new != nullptr) {
-    n = p_new + 1;
-  } else if (kv_len != nullptr) {
-    n = kv_len[b];
-  }
-  n = n < 0 ? 0 : (n > max_kv_len ? max_kv_len : n);
-  const int nsplit = (n + chunk - 1) / chunk;  // splits holding live slots
-  const size_t out_row0 = (static_cast<size_t>(b) * n_head + static_cast<size_t>(g) * G) * D;
-
-  // Partials are split-major: entry (split, batch row, query head).
-  const size_t head_row0 = static_cast<size_t>(b) * n_head + static_cast<size_t>(g) * G;
-  const size_t part_row0 = static_cast<size_t>(split) * gridDim.z * n_head + head_row0;
-  if (split >= nsplit) {
-    if (direct) {           // empty prefix, output written here: the empty sum, a zero row
-      for (int idx = tid; idx < G * D; idx += kThreads) out[out_row0 + idx] = 0;
-    } else if (tid < G) {   // mark the split empty for the combine
-      part_ml[part_row0 + tid] = make_float2(kNegInf, 0.0f);
-    }
+  SplitRange r;
+  if (!begin_split<G>(r, k_cache, v_cache, kv_len, k_new, v_new, pos, out, part_ml, n_kv_head,
+                      capacity, max_kv_len, chunk, direct))
     return;
-  }
-  const int row_begin = split * chunk;
-  const int row_end = min(row_begin + chunk, n);
+  const int last_row = r.last_row;
+  const int p_new = r.p_new;
 
   uint4 qv[G][CH];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) qv[i][c] = load16(q + out_row0 + static_cast<size_t>(i) * D + 8 * sub + 64 * c);
+    for (int c = 0; c < CH; ++c) qv[i][c] = load16(q + r.out_row0 + static_cast<size_t>(i) * D + 8 * sub + 64 * c);
   }
 
   float m[G], l[G], acc[G][DPL];
@@ -284,16 +402,15 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     for (int d = 0; d < DPL; ++d) acc[i][d] = 0.0f;
   }
 
-  const uint16_t* kbase = k_cache + head_off + 8 * sub;
-  const uint16_t* vbase = v_cache + head_off + 8 * sub;
-  const uint16_t* knew = k_new != nullptr ? k_new + new_row + 8 * sub : kbase;
-  const uint16_t* vnew = v_new != nullptr ? v_new + new_row + 8 * sub : vbase;
+  const uint16_t* kbase = k_cache + r.head_off + 8 * sub;
+  const uint16_t* vbase = v_cache + r.head_off + 8 * sub;
+  const uint16_t* knew = k_new != nullptr ? k_new + r.new_row + 8 * sub : kbase;
+  const uint16_t* vnew = v_new != nullptr ? v_new + r.new_row + 8 * sub : vbase;
 
-  const int wave_first = row_begin + wave * kWaveRows;
-  const int span = row_end - wave_first;
+  const int wave_first = r.row_begin + wave * kWaveRows;
+  const int span = last_row + 1 - wave_first;
   const int ntiles = span > 0 ? (span + kTile - 1) / kTile : 0;  // same for the whole wave
   const int my_first = wave_first + grp;
-  const int last_row = row_end - 1;
 
   // Rows past the split's end are loaded from its last live row (always in
   // bounds and finite) and given zero weight, so no branch guards the loads.
@@ -305,11 +422,11 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     const bool has_new = p_new >= tile_row0 && p_new < tile_row0 + kWaveRows;
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      const int r = min(base + t * kRows, last_row);
-      const size_t off = static_cast<size_t>(r) * D;
+      const int row = min(base + t * kRows, last_row);
+      const size_t off = static_cast<size_t>(row) * D;
       const uint16_t* kp = kbase + off;
       const uint16_t* vp = vbase + off;
-      if (has_new && r == p_new) {
+      if (has_new && row == p_new) {
         kp = knew;
         vp = vnew;
       }
@@ -328,17 +445,19 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
       const bool valid = base + t * kRows <= last_row;
 #pragma unroll
       for (int i = 0; i < G; ++i) {
-        float s = 0.0f;
+        float sc = 0.0f;
 #pragma unroll
-        for (int c = 0; c < CH; ++c) s = dot8<E>(kr[t][c], qv[i][c], s);
-        s = lane_group_sum<L>(s);
-        x[t][i] = valid ? s * scale_log2 : kNegInf;
+        for (int c = 0; c < CH; ++c) sc = dot8<E>(kr[t][c], qv[i][c], sc);
+        sc = lane_group_sum<L>(sc);
+        x[t][i] = valid ? sc * scale_log2 : kNegInf;
       }
     }
-    // The reference m need not be the exact running maximum: weights
-    // exp2(x - m) up to 2^kRescaleSlack are harmless in fp32, so the
-    // accumulator is rescaled only when some lane group sees a score more
-    // than kRescaleSlack above its reference (always on its first live row).
+    // The reference m is one value per head for the whole wavefront, and it
+    // need not be the exact running maximum: weights exp2(x - m) up to
+    // 2^kRescaleSlack are harmless in fp32, so the accumulator is rescaled
+    // only when some row scores more than kRescaleSlack above the reference
+    // (always on the wave's first live rows). Only then is the tile maximum
+    // reduced across the lane groups.
     float mt[G];
     bool grow = false;
 #pragma unroll
@@ -351,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     if (__any(grow)) {
 #pragma unroll
       for (int i = 0; i < G; ++i) {
-        const float m_new = fmaxf(m[i], mt[i]);
+        const float m_new = fmaxf(m[i], across_groups<L, Max>(mt[i]));
         const float alpha = fast_exp2(m[i] - finite_ref(m_new));
         l[i] *= alpha;
 #pragma unroll
@@ -397,56 +516,19 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     }
   }
 
-  // Merge the lane groups of the wavefront (lanes equal modulo L hold the
-  // same dims of different rows): common maximum, then rescaled sums.
+  // Lanes equal modulo L hold the same dims of different rows, all relative
+  // to the same reference m: the wave's state is their plain sum.
+#pragma unroll
+  for (int i = 0; i < G; ++i) l[i] = across_groups<L, Sum>(l[i]);
+  constexpr int V = G * DPL;
+  float red[V];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
-    const float mw = across_groups<L, Max>(m[i]);
-    const float sc = fast_exp2(m[i] - finite_ref(mw));
-    l[i] = across_groups<L, Sum>(l[i] * sc);
 #pragma unroll
-    for (int d = 0; d < DPL; ++d) acc[i][d] = across_groups<L, Sum>(acc[i][d] * sc);
-    m[i] = mw;
+    for (int d = 0; d < DPL; ++d) red[i * DPL + d] = acc[i][d];
   }
-
-  // Merge the 4 wavefronts through LDS.
-  __shared__ float s_acc[kWaves][G][D];
-  __shared__ float2 s_ml[kWaves][G];
-  if (lane < L) {
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-#pragma unroll
-        for (int d = 0; d < 8; ++d) s_acc[wave][i][8 * sub + 64 * c + d] = acc[i][8 * c + d];
-      }
-      if (lane == 0) s_ml[wave][i] = make_float2(m[i], l[i]);
-    }
-  }
-  __syncthreads();
-
-  for (int idx = tid; idx < G * D; idx += kThreads) {
-    const int i = idx / D;
-    const int d = idx % D;
-    float mw = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) mw = fmaxf(mw, s_ml[w][i].x);
-    const float ref = finite_ref(mw);
-    float lsum = 0.0f, o = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float wt = fast_exp2(s_ml[w][i].x - ref);
-      lsum += s_ml[w][i].y * wt;
-      o += s_acc[w][i][d] * wt;
-    }
-    if (direct) {
-      out[out_row0 + idx] = E::round(o / lsum);
-    } else {
-      const size_t pr = part_row0 + i;
-      part_acc[pr * D + d] = o;
-      if (d == 0) part_ml[pr] = make_float2(mw, lsum);
-    }
-  }
+  sum_lane_groups<L, V>(red, lane);
+  finish_split<E, G, L>(r, m, l, red, out, part_ml, part_acc, direct);
 }
 
 // Buffer resource over a workspace array: 32-bit byte offsets instead of
@@ -576,13 +658,16 @@ hipError_t launch_partial_g(const DecodeLaunch& p) {
     part_ml = reinterpret_cast<float2*>(base + w.ml_offset);
     part_acc = reinterpret_cast<float*>(base + w.acc_offset);
   }
-  hipLaunchKernelGGL((partial_kernel<E, G, C::L, C::T, C::P>), dim3(p.splits, p.n_kv_head, p.batch),
-                     dim3(kThreads), 0, p.stream, static_cast<const uint16_t*>(p.q),
-                     static_cast<uint16_t*>(const_cast<void*>(p.k_cache)),
-                     static_cast<uint16_t*>(const_cast<void*>(p.v_cache)), p.kv_len,
-                     static_cast<const uint16_t*>(p.k_new), static_cast<const uint16_t*>(p.v_new), p.pos,
-                     static_cast<uint16_t*>(p.out), part_ml, part_acc, p.n_kv_head,
-                     p.capacity, p.max_kv_len, p.chunk, p.direct ? 1 : 0, p.scale_log2);
+  const dim3 grid(p.splits, p.n_kv_head, p.batch);
+  const uint16_t* q = static_cast<const uint16_t*>(p.q);
+  uint16_t* k_cache = static_cast<uint16_t*>(const_cast<void*>(p.k_cache));
+  uint16_t* v_cache = static_cast<uint16_t*>(const_cast<void*>(p.v_cache));
+  const uint16_t* k_new = static_cast<const uint16_t*>(p.k_new);
+  const uint16_t* v_new = static_cast<const uint16_t*>(p.v_new);
+  uint16_t* out = static_cast<uint16_t*>(p.out);
+  hipLaunchKernelGGL((partial_kernel<E, G, C::L, C::T, C::P>), grid, dim3(kThreads), 0, p.stream, q, k_cache,
+                     v_cache, p.kv_len, k_new, v_new, p.pos, out, part_ml, part_acc, p.n_kv_head, p.capacity,
+                     p.max_kv_len, p.chunk, p.direct ? 1 : 0, p.scale_log2);
   return hipGetLastError();
 }
 
