@@ -5,6 +5,10 @@ this package. It wraps ``liboracle.so``, built from ``ada_oracle.c`` with the
 host C compiler, through ctypes. It shares no code with the GPU library and
 imports nothing from it.
 
+The rotary map applied to the new token's query and key before the cache
+write lives in ``rope.py`` (plain Python, exact rationals); ``decode_step_rope``
+below composes it with the append and the decode in the page's order.
+
 The C source states the definition it computes and the page sections it
 follows. Every function is pinned by ``tests/test_oracle_pins.py`` to results
 obtained another way (an independent library attention routine, closed forms,
@@ -141,6 +145,37 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle kv_append failed with status {rc}")
         return kc, vc
+
+
+def decode_step_rope(ora: "Oracle", q, k_new, v_new, cos, sin, k_cache, v_cache, pos, scale: float,
+                     dtype: str | None = None):
+    """One decode step with rotary embedding, in the order of the MiniCPM4
+    forward_step ("VoxCPM #395", section 4): rotate the new query and key
+    (``rope.rope``), write the rotated key and the value at slot pos[b] of
+    every KV head, then attend over slots [0, pos[b]] (kv_len = pos[b] + 1,
+    clamped to the capacity by the decode; a position outside the cache
+    writes nothing).
+
+    q [B, Hq, D], k_new / v_new [B, Hkv, D], cos / sin [B, D], caches
+    [B, Hkv, S, D] (16-bit tensors or uint16 patterns). Returns (out float64
+    [B, Hq, D], q_rot bits, k_cache bits, v_cache bits); the inputs are not
+    modified.
+    """
+    from . import rope as _rope
+
+    dt = _dtype_name(q, dtype)
+    qb = _bits(q)
+    if qb.ndim == 4:
+        qb = qb.reshape(qb.shape[0], qb.shape[1], qb.shape[3])
+    batch = qb.shape[0]
+    kn = _bits(k_new).reshape(batch, -1, qb.shape[-1])
+    q_rot = _rope.rope(qb, _bits(cos), _bits(sin), dt)
+    k_rot = _rope.rope(kn, _bits(cos), _bits(sin), dt)
+    kc, vc = ora.kv_append(k_rot, _bits(v_new), _bits(k_cache), _bits(v_cache), pos)
+    p = np.asarray(pos.cpu().numpy() if hasattr(pos, "cpu") else pos, dtype=np.int64).reshape(batch)
+    lens = np.clip(p + 1, 0, None).astype(np.int32)
+    out = ora.decode(q_rot, kc, vc, lens, scale, dt)
+    return out, q_rot, kc, vc
 
 
 _DEFAULT: Oracle | None = None

@@ -138,6 +138,20 @@ def append_inputs(batch: int, n_kv_head: int, head_dim: int, dtype: str, seed: i
     return k_new, v_new
 
 
+def rope_tables(positions, head_dim: int, dtype: str, base: float = 10000.0, device="cpu"):
+    """cos / sin rows [B, D] for the given per-row positions, rotate-half layout.
+
+    Angles pos * base^(-2i/D) for i < D/2, repeated in both halves (the usual
+    rotary frequencies; the pages do not give the model's own, so these are a
+    synthetic stand-in), evaluated in float64 and rounded to the 16-bit dtype.
+    """
+    pos = torch.as_tensor(positions, dtype=torch.float64).reshape(-1, 1)
+    inv = base ** (-torch.arange(0, head_dim, 2, dtype=torch.float64) / head_dim)
+    theta = torch.cat([pos * inv, pos * inv], dim=1)
+    dt = TORCH_DTYPES[dtype]
+    return torch.cos(theta).to(dt).to(device), torch.sin(theta).to(dt).to(device)
+
+
 def ragged_lengths(batch: int, low: int, high: int, seed: int) -> list:
     """Per-row kv_len drawn uniformly from [low, high], seeded."""
     g = torch.Generator().manual_seed(seed)
