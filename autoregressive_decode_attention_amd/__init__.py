@@ -46,7 +46,7 @@ EXPORTS = (
     "ada_abi_version", "ada_status_string", "ada_last_hip_error", "ada_device_num_cus",
     "ada_kv_append", "ada_decode_num_splits", "ada_decode_workspace_bytes",
     "ada_decode_attn_gqa", "ada_decode_attn_gqa_ex", "ada_decode_partial", "ada_decode_combine",
-    "ada_decode_step",
+    "ada_decode_step", "ada_rope_kv_append", "ada_decode_step_rope",
 )
 
 
@@ -82,6 +82,9 @@ def _declare(lib):
                                c_int),
         "ada_decode_step": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                              c_int, c_int, c_float, c_int, c_void_p, c_void_p, c_size_t, c_void_p, c_int], c_int),
+        "ada_rope_kv_append": ([c_void_p] * 9 + [c_int] * 6 + [c_void_p], c_int),
+        "ada_decode_step_rope": ([c_void_p] * 8 + [c_int] * 6 + [c_float, c_int, c_void_p, c_void_p, c_size_t,
+                                                                 c_void_p, c_int], c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -342,7 +345,65 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cac
     of the caches, then attend over slots 0..pos (kv_len = pos + 1). ``pos``:
     a host int (every row at that slot), host ints, or an int32 GPU tensor
     (then ``max_pos`` bounds it, default the last slot)."""
+    return _decode_step(q, k_new, v_new, None, None, k_cache, v_cache, pos, scale, out, max_pos, num_splits,
+                        workspace)
+
+
+def decode_step_rope(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cos: torch.Tensor,
+                     sin: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, pos, scale: float | None = None,
+                     out: torch.Tensor | None = None, max_pos: int | None = None, num_splits: int = 0,
+                     workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """decode_step with the rotary embedding of ``rope_kv_append`` applied to q
+    and k_new first (cos / sin: [B, D] tables in the cache dtype, row b for
+    batch row b's position). q is not modified."""
+    return _decode_step(q, k_new, v_new, cos, sin, k_cache, v_cache, pos, scale, out, max_pos, num_splits,
+                        workspace)
+
+
+def _check_tables(cos, sin, B, D, like):
+    for name, t in (("cos", cos), ("sin", sin)):
+        _require(isinstance(t, torch.Tensor) and t.dtype == like.dtype and t.device == like.device
+                 and t.is_contiguous() and t.numel() == B * D,
+                 f"{name} must be a contiguous [B, D] tensor in {like.dtype} on {like.device}")
+
+
+def rope_kv_append(q, k_new: torch.Tensor, v_new: torch.Tensor, cos: torch.Tensor, sin: torch.Tensor,
+                   k_cache: torch.Tensor, v_cache: torch.Tensor, pos, q_out: torch.Tensor | None = None):
+    """Rotate q [B, Hq, D] into q_out (allocated when None; may be q itself)
+    and k_new [B, Hkv, D] with the rotate-half rotary map, then write the
+    rotated key and v_new at slot pos[b] of the caches [B, Hkv, S, D]. ``q``
+    may be None (keys only). ``pos``: int32 GPU tensor [B] or host ints.
+    Returns q_out (None when q is None)."""
+    _require(k_cache.is_cuda and k_cache.dim() == 4, "k_cache must be a 4-d GPU tensor [B, Hkv, S, D]")
+    B, Hkv, S, D = k_cache.shape
+    _require(v_cache.shape == k_cache.shape, "v_cache shape must equal k_cache shape")
+    _require(k_cache.dtype in _DTYPE_CODES, "dtype must be float16 or bfloat16")
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _require(t.dtype == k_cache.dtype and t.device == k_cache.device and t.is_contiguous(),
+                 f"{name} must be contiguous, on {k_cache.device}, dtype {k_cache.dtype}")
+    _require(k_new.numel() == B * Hkv * D and v_new.numel() == B * Hkv * D, "k_new/v_new must be [B, Hkv, D]")
+    _check_tables(cos, sin, B, D, k_cache)
+    Hq = 0
+    if q is not None:
+        _require(q.dtype == k_cache.dtype and q.device == k_cache.device and q.is_contiguous()
+                 and q.shape[0] == B and q.shape[-1] == D and q.numel() % (B * D) == 0,
+                 "q must be a contiguous [B, Hq, D] tensor like the cache")
+        Hq = q.numel() // (B * D)
+        if q_out is None:
+            q_out = torch.empty_like(q)
+        _require(q_out.shape == q.shape and q_out.dtype == q.dtype and q_out.is_contiguous(), "q_out must be like q")
+    pos_t = _as_int32(pos, B, k_cache.device)
+    _check(_lib.ada_rope_kv_append(_ptr(q), _ptr(q_out), _ptr(k_new), _ptr(v_new), _ptr(cos), _ptr(sin),
+                                   _ptr(k_cache), _ptr(v_cache), _ptr(pos_t), B, Hq, Hkv, S, D,
+                                   _DTYPE_CODES[k_cache.dtype], ctypes.c_void_p(_stream(k_cache.device))),
+           "ada_rope_kv_append")
+    return q_out
+
+
+def _decode_step(q, k_new, v_new, cos, sin, k_cache, v_cache, pos, scale, out, max_pos, num_splits, workspace):
     B, Hq, Hkv, S, D = _check_decode_inputs(q, k_cache, v_cache)
+    if cos is not None or sin is not None:
+        _check_tables(cos, sin, B, D, k_cache)
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         _require(t.dtype == k_cache.dtype and t.device == k_cache.device and t.is_contiguous()
                  and t.numel() == B * Hkv * D, f"{name} must be a contiguous [B, Hkv, D] tensor like the cache")
@@ -370,10 +431,17 @@ def decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, k_cac
     ws = workspace if workspace is not None else _workspace(k_cache.device, need)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    rc = _lib.ada_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(pos_t), B, Hq,
-                              Hkv, D, S, mp, ctypes.c_float(scale), _DTYPE_CODES[k_cache.dtype], _ptr(out), _ptr(ws),
-                              ws_bytes, ctypes.c_void_p(_stream(k_cache.device)), int(num_splits))
-    _check(rc, "ada_decode_step")
+    if cos is None:
+        rc = _lib.ada_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(pos_t), B,
+                                  Hq, Hkv, D, S, mp, ctypes.c_float(scale), _DTYPE_CODES[k_cache.dtype], _ptr(out),
+                                  _ptr(ws), ws_bytes, ctypes.c_void_p(_stream(k_cache.device)), int(num_splits))
+        _check(rc, "ada_decode_step")
+    else:
+        rc = _lib.ada_decode_step_rope(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cos), _ptr(sin), _ptr(k_cache),
+                                       _ptr(v_cache), _ptr(pos_t), B, Hq, Hkv, D, S, mp, ctypes.c_float(scale),
+                                       _DTYPE_CODES[k_cache.dtype], _ptr(out), _ptr(ws), ws_bytes,
+                                       ctypes.c_void_p(_stream(k_cache.device)), int(num_splits))
+        _check(rc, "ada_decode_step_rope")
     return out
 
 
@@ -392,7 +460,8 @@ def decode_attn_gqa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
 
 __all__ = [
     "AdaError", "F16", "BF16", "HEAD_DIM", "MAX_SPLITS", "EXPORTS", "LIB_PATH", "load_library",
-    "kv_append", "decode_attn_gqa", "decode_attn_gqa_ex", "decode_partial", "decode_combine", "decode_step", "decode_num_splits", "decode_workspace_bytes",
+    "kv_append", "decode_attn_gqa", "decode_attn_gqa_ex", "decode_partial", "decode_combine", "decode_step", "decode_step_rope",
+    "rope_kv_append", "decode_num_splits", "decode_workspace_bytes",
     "new_workspace", "workspace_layout", "device_num_cus", "status_string", "last_hip_error",
     "abi_version",
 ]

@@ -159,6 +159,27 @@ int ada_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_c
   return e == hipSuccess ? ADA_OK : hip_fail(e);
 }
 
+int ada_rope_kv_append(const void* q, void* q_out, const void* k_new, const void* v_new, const void* cos,
+                       const void* sin, void* k_cache, void* v_cache, const int32_t* pos, int batch,
+                       int n_head, int n_kv_head, int capacity, int head_dim, int dtype, void* stream) {
+  if (dtype != ADA_F16 && dtype != ADA_BF16) return ADA_ERR_DTYPE;
+  if (batch < 0 || n_kv_head <= 0 || capacity <= 0 || n_head < 0) return ADA_ERR_SHAPE;
+  if (head_dim != ada::kHeadDim) return ADA_ERR_HEAD_DIM;
+  if ((q == nullptr) != (q_out == nullptr)) return ADA_ERR_NULL;
+  if (q != nullptr && n_head <= 0) return ADA_ERR_SHAPE;
+  const int64_t rows = static_cast<int64_t>(batch) * ((q ? n_head : 0) + n_kv_head);
+  if (rows * 16 > INT32_MAX - 255) return ADA_ERR_SHAPE;
+  if (batch == 0) return ADA_OK;
+  if (!k_new || !v_new || !cos || !sin || !k_cache || !v_cache || !pos) return ADA_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(cos) || !aligned16(sin) ||
+      !aligned16(k_cache) || !aligned16(v_cache) || (q && (!aligned16(q) || !aligned16(q_out))))
+    return ADA_ERR_ALIGN;
+  hipError_t e = ada::launch_rope_kv_append(q, q_out, k_new, v_new, cos, sin, k_cache, v_cache, pos, batch,
+                                            n_head, n_kv_head, capacity, dtype,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ADA_OK : hip_fail(e);
+}
+
 }  // extern "C"
 
 namespace {
@@ -258,10 +279,14 @@ int ada_decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache,
                                 workspace_bytes, stream, 0);
 }
 
-int ada_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                    const int32_t* pos, int batch, int n_head, int n_kv_head, int head_dim,
-                    int capacity, int max_pos, float scale, int dtype, void* out, void* workspace,
-                    size_t workspace_bytes, void* stream, int num_splits) {
+}  // extern "C"
+
+namespace {
+
+int decode_step_impl(const void* q, const void* k_new, const void* v_new, const void* cos, const void* sin,
+                     void* k_cache, void* v_cache, const int32_t* pos, int batch, int n_head, int n_kv_head,
+                     int head_dim, int capacity, int max_pos, float scale, int dtype, void* out,
+                     void* workspace, size_t workspace_bytes, void* stream, int num_splits) {
   if (max_pos < 0 || max_pos >= capacity) {
     if (dtype != ADA_F16 && dtype != ADA_BF16) return ADA_ERR_DTYPE;
     return ADA_ERR_SHAPE;
@@ -272,9 +297,13 @@ int ada_decode_step(const void* q, const void* k_new, const void* v_new, void* k
   if (rc != ADA_OK || batch == 0) return rc;
   if (!k_new || !v_new || !out) return ADA_ERR_NULL;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(out)) return ADA_ERR_ALIGN;
+  if ((cos == nullptr) != (sin == nullptr)) return ADA_ERR_NULL;
+  if (cos && (!aligned16(cos) || !aligned16(sin))) return ADA_ERR_ALIGN;
   p.k_new = k_new;
   p.v_new = v_new;
   p.pos = pos;
+  p.cos = cos;
+  p.sin = sin;
   p.out = out;
   p.direct = p.splits == 1;
   if (!p.direct) {
@@ -288,6 +317,31 @@ int ada_decode_step(const void* q, const void* k_new, const void* v_new, void* k
   ada::CombineLaunch c{workspace, out, batch, n_head, n_kv_head, p.splits, dtype, p.stream};
   e = ada::launch_combine(c);
   return e == hipSuccess ? ADA_OK : hip_fail(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ada_decode_step(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                    const int32_t* pos, int batch, int n_head, int n_kv_head, int head_dim,
+                    int capacity, int max_pos, float scale, int dtype, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream, int num_splits) {
+  return decode_step_impl(q, k_new, v_new, nullptr, nullptr, k_cache, v_cache, pos, batch, n_head, n_kv_head,
+                          head_dim, capacity, max_pos, scale, dtype, out, workspace, workspace_bytes, stream,
+                          num_splits);
+}
+
+int ada_decode_step_rope(const void* q, const void* k_new, const void* v_new, const void* cos, const void* sin,
+                         void* k_cache, void* v_cache, const int32_t* pos, int batch, int n_head, int n_kv_head,
+                         int head_dim, int capacity, int max_pos, float scale, int dtype, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream, int num_splits) {
+  if (!cos || !sin) {
+    if (dtype != ADA_F16 && dtype != ADA_BF16) return ADA_ERR_DTYPE;
+    if (batch > 0) return ADA_ERR_NULL;
+  }
+  return decode_step_impl(q, k_new, v_new, cos, sin, k_cache, v_cache, pos, batch, n_head, n_kv_head, head_dim,
+                          capacity, max_pos, scale, dtype, out, workspace, workspace_bytes, stream, num_splits);
 }
 
 int ada_decode_partial(const void* q, const void* k_cache, const void* v_cache,

@@ -38,6 +38,8 @@ struct DecodeLaunch {
   const void* k_new;    // decode step: new rows appended at pos (else NULL)
   const void* v_new;
   const int32_t* pos;   // decode step: device slots, or NULL (slot max_kv_len - 1)
+  const void* cos;      // decode step with rotary embedding: [B, D] tables (else NULL)
+  const void* sin;
   void* out;        // written when direct
   void* workspace;  // partials written when !direct
   int batch, n_head, n_kv_head, capacity, max_kv_len;
@@ -58,6 +60,11 @@ struct CombineLaunch {
 
 hipError_t launch_partial(const DecodeLaunch& p);
 hipError_t launch_combine(const CombineLaunch& p);
+
+hipError_t launch_rope_kv_append(const void* q, void* q_out, const void* k_new, const void* v_new,
+                                 const void* cos, const void* sin, void* k_cache, void* v_cache,
+                                 const int32_t* pos, int batch, int n_head, int n_kv_head, int capacity,
+                                 int dtype, hipStream_t stream);
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             const int32_t* pos, int batch, int n_kv_head, int capacity,

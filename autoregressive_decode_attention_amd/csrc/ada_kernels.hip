@@ -186,6 +186,69 @@ __device__ __forceinline__ float dot8(const uint4& k, const uint4& q, float s) {
 }
 
 // ---------------------------------------------------------------------------
+// Rotary embedding of the new token's query and key before the cache write
+// ([FORWARD-STEP] section 4 applies apply_rotary_pos_emb there; it is read
+// as the rotate-half form): with h = D / 2,
+//   out[i] = x[i] cos[i] - x[i + h] sin[i]    (i <  h)
+//   out[i] = x[i] cos[i] + x[i - h] sin[i]    (i >= h)
+// over the stored 16-bit values, rounded once to the 16-bit format (nearest,
+// ties to even; a zero result is +0).
+//
+// Both products are exact in fp32 (two 8- or 11-bit significands; inputs
+// whose products fall below fp32's normal range are the exception). The sum
+// is formed with its exact rounding error (Knuth's two-sum), and the fp32
+// result is then rounded to odd: an inexact sum moves to the neighbour with
+// an odd last bit on the side of the exact value. An fp32 value rounded to
+// odd keeps enough information for the final round-to-nearest-even to 16
+// bits (13 or 16 fewer significand bits) to give the correctly rounded
+// result of the exact sum.
+template <class E>
+__device__ __forceinline__ uint32_t round_sum(float a, float b) {
+  const float s = a + b;
+  const float bv = s - a;
+  const float av = s - bv;
+  const float err = (a - av) + (b - bv);
+  uint32_t bits = __float_as_uint(s);
+  if (err != 0.0f && __builtin_isfinite(s)) {
+    if ((err < 0.0f) != (s < 0.0f)) bits -= 1u;  // truncate toward zero...
+    bits |= 1u;                                  // ...then force the last bit odd
+  }
+  const uint32_t r = E::round(__uint_as_float(bits));
+  return (r & 0x7fffu) == 0 ? 0u : r;
+}
+
+// Rotate 8 consecutive dims [d0, d0 + 8) of a head: x holds them, partner the
+// dims h away (d0 +- h), c and s the table entries of [d0, d0 + 8).
+template <class E>
+__device__ __forceinline__ uint4 rope8(const uint4& x, const uint4& partner, const uint4& c, const uint4& s,
+                                       bool first_half) {
+  float xf[8], pf[8], cf[8], sf[8];
+  unpack8<E>(x, xf);
+  unpack8<E>(partner, pf);
+  unpack8<E>(c, cf);
+  unpack8<E>(s, sf);
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float p0 = pf[2 * k] * sf[2 * k];
+    const float p1 = pf[2 * k + 1] * sf[2 * k + 1];
+    const uint32_t lo = round_sum<E>(xf[2 * k] * cf[2 * k], first_half ? -p0 : p0);
+    const uint32_t hi = round_sum<E>(xf[2 * k + 1] * cf[2 * k + 1], first_half ? -p1 : p1);
+    w[k] = lo | (hi << 16);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Rotated 16-byte chunk at dims [d0, d0 + 8) of the head starting at `row`,
+// with the table row `cs` / `sn` (D entries each).
+template <class E>
+__device__ __forceinline__ uint4 rope_chunk(const uint16_t* row, const uint16_t* cs, const uint16_t* sn, int d0) {
+  constexpr int H = kHeadDim / 2;
+  const int partner = d0 < H ? d0 + H : d0 - H;
+  return rope8<E>(load16(row + d0), load16(row + partner), load16(cs + d0), load16(sn + d0), d0 < H);
+}
+
+// ---------------------------------------------------------------------------
 // Partial kernels: shared prologue and epilogue.
 
 // Where one workgroup stands: its split's live slot range and the indices of
@@ -211,12 +274,13 @@ struct SplitRange {
 // Returns false when the split holds no live slot; it has then written what
 // an empty split owes (a zero row when writing the output directly, an
 // "empty" mark for the combine otherwise).
-template <int G>
+template <class E, int G, bool R>
 __device__ __forceinline__ bool begin_split(SplitRange& r, uint16_t* k_cache, uint16_t* v_cache,
                                             const int32_t* kv_len, const uint16_t* k_new,
-                                            const uint16_t* v_new, const int32_t* pos, uint16_t* out,
-                                            float2* part_ml, int n_kv_head, int capacity,
-                                            int max_kv_len, int chunk, int direct) {
+                                            const uint16_t* v_new, const int32_t* pos, const uint16_t* cs,
+                                            const uint16_t* sn, uint16_t* out, float2* part_ml,
+                                            int n_kv_head, int capacity, int max_kv_len, int chunk,
+                                            int direct) {
   constexpr int D = kHeadDim;
   const int split = blockIdx.x;
   const int g = blockIdx.y;
@@ -232,7 +296,13 @@ __device__ __forceinline__ bool begin_split(SplitRange& r, uint16_t* k_cache, ui
       const int c = 8 * (tid & 15);  // one 16-byte chunk of the key (tid < 16) or value row
       const size_t dst = r.head_off + static_cast<size_t>(r.p_new) * D + c;
       if (tid < 16) {
-        *reinterpret_cast<uint4*>(k_cache + dst) = load16(k_new + r.new_row + c);
+        uint4 kv;
+        if constexpr (R) {
+          kv = rope_chunk<E>(k_new + r.new_row, cs + static_cast<size_t>(b) * D, sn + static_cast<size_t>(b) * D, c);
+        } else {
+          kv = load16(k_new + r.new_row + c);
+        }
+        *reinterpret_cast<uint4*>(k_cache + dst) = kv;
       } else {
         *reinterpret_cast<uint4*>(v_cache + dst) = load16(v_new + r.new_row + c);
       }
@@ -358,11 +428,12 @@ __device__ __forceinline__ void finish_split(const SplitRange& r, const float (&
 //   T  rows per lane group per tile
 //   P  tiles in flight ahead of the one being computed (register ring of
 //      P + 1 tiles; the ring is unrolled so buffers never move)
-template <class E, int G, int L, int T, int P>
+template <class E, int G, int L, int T, int P, bool R>
 __global__ __launch_bounds__(kThreads) void partial_kernel(
     const uint16_t* __restrict__ q, uint16_t* k_cache, uint16_t* v_cache,
     const int32_t* __restrict__ kv_len, const uint16_t* __restrict__ k_new,
     const uint16_t* __restrict__ v_new, const int32_t* __restrict__ pos,
+    const uint16_t* __restrict__ cs, const uint16_t* __restrict__ sn,
     uint16_t* __restrict__ out, float2* __restrict__ part_ml, float* __restrict__ part_acc,
     int n_kv_head, int capacity, int max_kv_len, int chunk, int direct, float scale_log2) {
   constexpr int D = kHeadDim;
@@ -380,17 +451,30 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   const int sub = lane % L;   // dims [8*sub, +8) (and [64 + 8*sub, +8) when L == 8)
 
   SplitRange r;
-  if (!begin_split<G>(r, k_cache, v_cache, kv_len, k_new, v_new, pos, out, part_ml, n_kv_head,
-                      capacity, max_kv_len, chunk, direct))
+  if (!begin_split<E, G, R>(r, k_cache, v_cache, kv_len, k_new, v_new, pos, cs, sn, out, part_ml,
+                            n_kv_head, capacity, max_kv_len, chunk, direct))
     return;
   const int last_row = r.last_row;
   const int p_new = r.p_new;
 
+  // With rotary tables (a decode step with rotary embedding) the query and
+  // the new key are rotated here, each lane its own chunks; the rotated key
+  // replaces the loaded row in the tile that holds slot p_new.
+  const uint16_t* cs_row = R ? cs + static_cast<size_t>(blockIdx.z) * D : nullptr;
+  const uint16_t* sn_row = R ? sn + static_cast<size_t>(blockIdx.z) * D : nullptr;
   uint4 qv[G][CH];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) qv[i][c] = load16(q + r.out_row0 + static_cast<size_t>(i) * D + 8 * sub + 64 * c);
+    for (int c = 0; c < CH; ++c) {
+      const uint16_t* qrow = q + r.out_row0 + static_cast<size_t>(i) * D;
+      qv[i][c] = R ? rope_chunk<E>(qrow, cs_row, sn_row, 8 * sub + 64 * c) : load16(qrow + 8 * sub + 64 * c);
+    }
+  }
+  uint4 krot[R ? CH : 1];
+  if constexpr (R) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) krot[c] = rope_chunk<E>(k_new + r.new_row, cs_row, sn_row, 8 * sub + 64 * c);
   }
 
   float m[G], l[G], acc[G][DPL];
@@ -438,7 +522,25 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
     }
   };
 
-  auto process = [&](int base, const uint4 (&kr)[T][CH], const uint4 (&vr)[T][CH]) {
+  auto process = [&](int base, const uint4 (&kr_in)[T][CH], const uint4 (&vr)[T][CH]) {
+    uint4 kr[T][CH];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) kr[t][c] = kr_in[t][c];
+    }
+    if constexpr (R) {
+      const int tile_row0 = base - grp;
+      if (p_new >= tile_row0 && p_new < tile_row0 + kWaveRows) {  // uniform across the wave
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          if (min(base + t * kRows, last_row) == p_new) {
+#pragma unroll
+            for (int c = 0; c < CH; ++c) kr[t][c] = krot[c];
+          }
+        }
+      }
+    }
     float x[T][G];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
@@ -633,6 +735,41 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint4* __restrict_
   v_cache[dst] = v_new[static_cast<size_t>(row) * kChunks + c];
 }
 
+// Rotary embedding of the new token's query and key, and the append of the
+// rotated key and the value at slot pos[b] ([FORWARD-STEP] section 4): 16
+// lanes per 128-element row, one 16-byte chunk each. Rows [0, B*Hq) are query
+// heads (q -> q_out, which may be q itself: a lane reads both chunks it needs
+// before the wave writes), rows [B*Hq, B*Hq + B*Hkv) are KV heads. A slot
+// outside [0, capacity) writes nothing to the cache.
+template <class E>
+__global__ __launch_bounds__(256) void rope_append_kernel(
+    const uint16_t* q, uint16_t* q_out, const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, const uint16_t* __restrict__ cs, const uint16_t* __restrict__ sn,
+    uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache, const int32_t* __restrict__ pos,
+    int n_head, int n_kv_head, int capacity, int q_rows, int rows) {
+  constexpr int D = kHeadDim;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  const int row = idx / 16;
+  const int d0 = 8 * (idx % 16);
+  if (row >= rows) return;
+  if (row < q_rows) {
+    const int b = row / n_head;
+    const size_t off = static_cast<size_t>(row) * D;
+    const uint4 v = rope_chunk<E>(q + off, cs + static_cast<size_t>(b) * D, sn + static_cast<size_t>(b) * D, d0);
+    *reinterpret_cast<uint4*>(q_out + off + d0) = v;
+    return;
+  }
+  const int kr = row - q_rows;  // b * n_kv_head + h
+  const int b = kr / n_kv_head;
+  const int p = pos[b];
+  if (p < 0 || p >= capacity) return;
+  const size_t src = static_cast<size_t>(kr) * D;
+  const size_t dst = (static_cast<size_t>(kr) * capacity + p) * D + d0;
+  const uint4 k = rope_chunk<E>(k_new + src, cs + static_cast<size_t>(b) * D, sn + static_cast<size_t>(b) * D, d0);
+  *reinterpret_cast<uint4*>(k_cache + dst) = k;
+  *reinterpret_cast<uint4*>(v_cache + dst) = load16(v_new + src + d0);
+}
+
 // Per group size: lanes per row L, rows per lane group per tile T, tiles in
 // flight P. Every choice gives 64-row workgroup tiles, the granularity the
 // split heuristic rounds to.
@@ -665,9 +802,17 @@ hipError_t launch_partial_g(const DecodeLaunch& p) {
   const uint16_t* k_new = static_cast<const uint16_t*>(p.k_new);
   const uint16_t* v_new = static_cast<const uint16_t*>(p.v_new);
   uint16_t* out = static_cast<uint16_t*>(p.out);
-  hipLaunchKernelGGL((partial_kernel<E, G, C::L, C::T, C::P>), grid, dim3(kThreads), 0, p.stream, q, k_cache,
-                     v_cache, p.kv_len, k_new, v_new, p.pos, out, part_ml, part_acc, p.n_kv_head, p.capacity,
-                     p.max_kv_len, p.chunk, p.direct ? 1 : 0, p.scale_log2);
+  const uint16_t* cs = static_cast<const uint16_t*>(p.cos);
+  const uint16_t* sn = static_cast<const uint16_t*>(p.sin);
+  if (cs != nullptr) {
+    hipLaunchKernelGGL((partial_kernel<E, G, C::L, C::T, C::P, true>), grid, dim3(kThreads), 0, p.stream, q,
+                       k_cache, v_cache, p.kv_len, k_new, v_new, p.pos, cs, sn, out, part_ml, part_acc,
+                       p.n_kv_head, p.capacity, p.max_kv_len, p.chunk, p.direct ? 1 : 0, p.scale_log2);
+  } else {
+    hipLaunchKernelGGL((partial_kernel<E, G, C::L, C::T, C::P, false>), grid, dim3(kThreads), 0, p.stream, q,
+                       k_cache, v_cache, p.kv_len, k_new, v_new, p.pos, cs, sn, out, part_ml, part_acc,
+                       p.n_kv_head, p.capacity, p.max_kv_len, p.chunk, p.direct ? 1 : 0, p.scale_log2);
+  }
   return hipGetLastError();
 }
 
@@ -705,6 +850,28 @@ hipError_t launch_combine_impl(const CombineLaunch& p) {
 hipError_t launch_partial(const DecodeLaunch& p) { ADA_DISPATCH_GROUP(launch_partial_g, p) }
 
 hipError_t launch_combine(const CombineLaunch& p) { return launch_combine_impl(p); }
+
+hipError_t launch_rope_kv_append(const void* q, void* q_out, const void* k_new, const void* v_new,
+                                 const void* cos, const void* sin, void* k_cache, void* v_cache,
+                                 const int32_t* pos, int batch, int n_head, int n_kv_head, int capacity,
+                                 int dtype, hipStream_t stream) {
+  const int q_rows = q != nullptr ? batch * n_head : 0;
+  const int rows = q_rows + batch * n_kv_head;
+  const int blocks = (rows * 16 + 255) / 256;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), 0, stream, static_cast<const uint16_t*>(q),
+                       static_cast<uint16_t*>(q_out), static_cast<const uint16_t*>(k_new),
+                       static_cast<const uint16_t*>(v_new), static_cast<const uint16_t*>(cos),
+                       static_cast<const uint16_t*>(sin), static_cast<uint16_t*>(k_cache),
+                       static_cast<uint16_t*>(v_cache), pos, n_head, n_kv_head, capacity, q_rows, rows);
+  };
+  if (dtype == 1) {
+    go(rope_append_kernel<BF16>);
+  } else {
+    go(rope_append_kernel<F16>);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                             const int32_t* pos, int batch, int n_kv_head, int capacity,

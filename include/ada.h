@@ -102,6 +102,40 @@ int ada_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_c
                   int head_dim, int dtype, void* stream);
 
 /*
+ * Rotary embedding of the new token, then the append: [FORWARD-STEP] section
+ * 4 applies apply_rotary_pos_emb(query, key, cos, sin) to the step's query
+ * and key just before the key and value rows are written at position_id. The
+ * page names the function without printing it; it is read as the rotate-half
+ * form, per head of D values with h = D / 2:
+ *   out[i] = x[i] cos[i] - x[i + h] sin[i]    (i <  h)
+ *   out[i] = x[i] cos[i] + x[i - h] sin[i]    (i >= h)
+ * computed exactly from the stored 16-bit values and rounded once to the
+ * dtype (nearest, ties to even; a zero result is +0). Exact for inputs whose
+ * products x * cos, x * sin stay within fp32's normal range (always for
+ * fp16; bf16 magnitudes below about 1e-19 may round differently). Inputs
+ * must be finite.
+ *
+ *   q, q_out      device, [batch, n_head, head_dim]: q_out = rotated q. q_out
+ *                 may equal q (in place). Both NULL: keys only (n_head is
+ *                 then ignored); one NULL alone is ADA_ERR_NULL.
+ *   k_new, v_new  device, [batch, n_kv_head, head_dim]; k_new is rotated
+ *                 before the write, v_new is copied.
+ *   cos, sin      device, [batch, head_dim] in dtype: row b is the table of
+ *                 batch row b's position (the caller computes it, with any
+ *                 frequency scaling of its model).
+ *   k_cache,      device, [batch, n_kv_head, capacity, head_dim]; row pos[b]
+ *   v_cache       of every KV head of batch row b is written when
+ *                 0 <= pos[b] < capacity, else nothing is.
+ *   pos           device int32 [batch].
+ * All buffers 16-byte aligned (ADA_ERR_ALIGN); head_dim 128. Returns
+ * ADA_ERR_SHAPE for negative sizes or a launch too large to index, ADA_OK
+ * without work for batch == 0. One kernel launch on `stream`.
+ */
+int ada_rope_kv_append(const void* q, void* q_out, const void* k_new, const void* v_new, const void* cos,
+                       const void* sin, void* k_cache, void* v_cache, const int32_t* pos, int batch,
+                       int n_head, int n_kv_head, int capacity, int head_dim, int dtype, void* stream);
+
+/*
  * Split heuristic: number of key-range splits for a decode call over
  * batch * n_kv_head (batch row, KV head) units whose live prefixes are at
  * most max_kv_len slots, on a device with num_cus compute units. It aims at
@@ -208,6 +242,26 @@ int ada_decode_step(const void* q, const void* k_new, const void* v_new, void* k
                     const int32_t* pos, int batch, int n_head, int n_kv_head, int head_dim,
                     int capacity, int max_pos, float scale, int dtype, void* out, void* workspace,
                     size_t workspace_bytes, void* stream, int num_splits);
+
+/*
+ * ada_decode_step with the rotary embedding of ada_rope_kv_append applied to
+ * q and k_new first ([FORWARD-STEP] section 4: rotate, write the cache row at
+ * position_id, attend over slots 0..position_id with the rotated query).
+ * Equivalent to ada_rope_kv_append into a temporary rotated query, then
+ * ada_decode_attn_gqa with kv_len[b] = pos[b] + 1, in the launches of
+ * ada_decode_step: every workgroup rotates its own copy of the query, the
+ * workgroup of the first split writes the rotated key, and the workgroup
+ * whose key range holds slot pos[b] uses the rotated key it computed itself.
+ * q is not modified.
+ *
+ *   cos, sin  device, [batch, head_dim] in dtype, 16-byte aligned, both
+ *             required (ADA_ERR_NULL).
+ * Other arguments as ada_decode_step.
+ */
+int ada_decode_step_rope(const void* q, const void* k_new, const void* v_new, const void* cos, const void* sin,
+                         void* k_cache, void* v_cache, const int32_t* pos, int batch, int n_head, int n_kv_head,
+                         int head_dim, int capacity, int max_pos, float scale, int dtype, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream, int num_splits);
 
 /*
  * The two halves of a decode call, for callers that merge partial results

@@ -169,6 +169,44 @@ def test_decode_step_validation(ada):
     assert f(*args(splits=300)) == -8
 
 
+def test_rope_kv_append_validation(ada):
+    f = ada._lib.ada_rope_kv_append
+    # q, q_out, k_new, v_new, cos, sin, k_cache, v_cache, pos, B, Hq, Hkv, S, D, dtype, stream
+    args = lambda **kw: [kw.get("q", P), kw.get("qo", P2), kw.get("kn", P3), kw.get("vn", P4), kw.get("cos", P5),
+                         kw.get("sin", P), kw.get("kc", P2), kw.get("vc", P3), kw.get("pos", P4), kw.get("B", 1),
+                         kw.get("Hq", 32), 8, 16, kw.get("D", 128), kw.get("dtype", 0), NUL]
+    assert f(*args(dtype=3)) == -4
+    assert f(*args(D=64)) == -5
+    assert f(*args(B=-1)) == -2
+    assert f(*args(Hq=0)) == -2                  # a query needs heads
+    assert f(*args(qo=NUL)) == -1                # q without q_out
+    assert f(*args(q=NUL)) == -1                 # q_out without q
+    assert f(*args(cos=NUL)) == -1
+    assert f(*args(sin=NUL)) == -1
+    assert f(*args(pos=NUL)) == -1
+    assert f(*args(cos=MIS)) == -9
+    assert f(*args(qo=MIS)) == -9
+    assert f(*args(B=0, q=NUL, qo=NUL, kn=NUL, vn=NUL, cos=NUL, sin=NUL, kc=NUL, vc=NUL, pos=NUL)) == 0
+
+
+def test_decode_step_rope_validation(ada):
+    f = ada._lib.ada_decode_step_rope
+    args = lambda **kw: [kw.get("q", P), kw.get("kn", P2), kw.get("vn", P3), kw.get("cos", P4), kw.get("sin", P5),
+                         P, P2, NUL, 1, 32, 8, kw.get("D", 128), 2048, kw.get("mp", 399), ctypes.c_float(0.08),
+                         kw.get("dtype", 0), kw.get("out", P3), kw.get("ws", NUL), kw.get("ws_bytes", 0), NUL,
+                         kw.get("splits", 2)]
+    assert f(*args(cos=NUL)) == -1
+    assert f(*args(sin=NUL)) == -1
+    assert f(*args(cos=MIS)) == -9
+    assert f(*args(sin=MIS)) == -9
+    assert f(*args(dtype=7)) == -4
+    assert f(*args(mp=2048)) == -2
+    assert f(*args(D=64)) == -5
+    assert f(*args(kn=NUL)) == -1
+    assert f(*args()) == -7                      # two splits need a workspace
+    assert f(*args(splits=300)) == -8
+
+
 def test_workspace_bytes_arithmetic(ada):
     r256 = lambda x: (x + 255) // 256 * 256
     for B, Hq, Hkv, splits in ((1, 32, 8, 4), (8, 32, 8, 8), (4, 32, 8, 33), (1, 16, 16, 32), (3, 6, 3, 7)):
