@@ -274,13 +274,12 @@ struct SplitRange {
 // Returns false when the split holds no live slot; it has then written what
 // an empty split owes (a zero row when writing the output directly, an
 // "empty" mark for the combine otherwise).
-template <class E, int G, bool R>
+template <int G, bool R>
 __device__ __forceinline__ bool begin_split(SplitRange& r, uint16_t* k_cache, uint16_t* v_cache,
                                             const int32_t* kv_len, const uint16_t* k_new,
-                                            const uint16_t* v_new, const int32_t* pos, const uint16_t* cs,
-                                            const uint16_t* sn, uint16_t* out, float2* part_ml,
-                                            int n_kv_head, int capacity, int max_kv_len, int chunk,
-                                            int direct) {
+                                            const uint16_t* v_new, const int32_t* pos, uint16_t* out,
+                                            float2* part_ml, int n_kv_head, int capacity, int max_kv_len,
+                                            int chunk, int direct) {
   constexpr int D = kHeadDim;
   const int split = blockIdx.x;
   const int g = blockIdx.y;
@@ -296,13 +295,8 @@ __device__ __forceinline__ bool begin_split(SplitRange& r, uint16_t* k_cache, ui
       const int c = 8 * (tid & 15);  // one 16-byte chunk of the key (tid < 16) or value row
       const size_t dst = r.head_off + static_cast<size_t>(r.p_new) * D + c;
       if (tid < 16) {
-        uint4 kv;
-        if constexpr (R) {
-          kv = rope_chunk<E>(k_new + r.new_row, cs + static_cast<size_t>(b) * D, sn + static_cast<size_t>(b) * D, c);
-        } else {
-          kv = load16(k_new + r.new_row + c);
-        }
-        *reinterpret_cast<uint4*>(k_cache + dst) = kv;
+        // with rotary tables the rotated key is written once it is computed
+        if constexpr (!R) *reinterpret_cast<uint4*>(k_cache + dst) = load16(k_new + r.new_row + c);
       } else {
         *reinterpret_cast<uint4*>(v_cache + dst) = load16(v_new + r.new_row + c);
       }
@@ -451,30 +445,20 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   const int sub = lane % L;   // dims [8*sub, +8) (and [64 + 8*sub, +8) when L == 8)
 
   SplitRange r;
-  if (!begin_split<E, G, R>(r, k_cache, v_cache, kv_len, k_new, v_new, pos, cs, sn, out, part_ml,
-                            n_kv_head, capacity, max_kv_len, chunk, direct))
+  if (!begin_split<G, R>(r, k_cache, v_cache, kv_len, k_new, v_new, pos, out, part_ml, n_kv_head, capacity,
+                         max_kv_len, chunk, direct))
     return;
   const int last_row = r.last_row;
   const int p_new = r.p_new;
 
-  // With rotary tables (a decode step with rotary embedding) the query and
-  // the new key are rotated here, each lane its own chunks; the rotated key
-  // replaces the loaded row in the tile that holds slot p_new.
-  const uint16_t* cs_row = R ? cs + static_cast<size_t>(blockIdx.z) * D : nullptr;
-  const uint16_t* sn_row = R ? sn + static_cast<size_t>(blockIdx.z) * D : nullptr;
   uint4 qv[G][CH];
+  uint4 krot[R ? CH : 1];  // rotated new key (rotary tables only)
+  if constexpr (!R) {
 #pragma unroll
-  for (int i = 0; i < G; ++i) {
+    for (int i = 0; i < G; ++i) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const uint16_t* qrow = q + r.out_row0 + static_cast<size_t>(i) * D;
-      qv[i][c] = R ? rope_chunk<E>(qrow, cs_row, sn_row, 8 * sub + 64 * c) : load16(qrow + 8 * sub + 64 * c);
+      for (int c = 0; c < CH; ++c) qv[i][c] = load16(q + r.out_row0 + static_cast<size_t>(i) * D + 8 * sub + 64 * c);
     }
-  }
-  uint4 krot[R ? CH : 1];
-  if constexpr (R) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) krot[c] = rope_chunk<E>(k_new + r.new_row, cs_row, sn_row, 8 * sub + 64 * c);
   }
 
   float m[G], l[G], acc[G][DPL];
@@ -607,6 +591,33 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
   for (int pf = 0; pf < P; ++pf) {
     if (pf < ntiles) load_tile(my_first + pf * kTile, kb[pf], vb[pf]);
   }
+
+  // With rotary tables (a decode step with rotary embedding) the G query
+  // heads and the new key are rotated once per workgroup, one 16-byte chunk
+  // per thread, after the first tiles are on their way; the first split
+  // writes the rotated key into the cache, and the rotated key replaces the
+  // loaded row in the tile that holds slot p_new.
+  if constexpr (R) {
+    __shared__ uint4 s_rot[G + 1][16];  // [query heads..., new key][chunk]
+    if (tid < (G + 1) * 16) {
+      const int h = tid / 16;
+      const int c = tid % 16;
+      const uint16_t* row = h < G ? q + r.out_row0 + static_cast<size_t>(h) * D : k_new + r.new_row;
+      const uint4 v = rope_chunk<E>(row, cs + static_cast<size_t>(blockIdx.z) * D,
+                                    sn + static_cast<size_t>(blockIdx.z) * D, 8 * c);
+      s_rot[h][c] = v;
+      if (h == G && blockIdx.x == 0 && p_new >= 0 && p_new < capacity)
+        *reinterpret_cast<uint4*>(k_cache + r.head_off + static_cast<size_t>(p_new) * D + 8 * c) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) qv[i][c] = s_rot[i][sub + 8 * c];
+      krot[c] = s_rot[G][sub + 8 * c];
+    }
+  }
+
   for (int t0 = 0; t0 < ntiles; t0 += NB) {
 #pragma unroll
     for (int u = 0; u < NB; ++u) {

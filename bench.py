@@ -15,9 +15,10 @@ over the timed steps), the roofline of the dominant kernel (the split-KV
 partial: algorithmic bytes / its average duration over back-to-back launches
 bracketed by HIP events, with the host queued ahead so that launch cost does
 not count, against 8 TB/s), the fp64 CPU oracle timed on a bounded sample of
-the same step, and, under "also", the per-kv_len figures and the
+the same step, and, under "also", the per-kv_len figures, the
 long-context workload (batch 8, 32/8 heads, bf16, kv_len 32768, 1.07 GB per
-call).
+call), the 36-layer S2-Pro-shaped run, the full-capacity against
+active-prefix comparison, and the decode step with rotary embedding.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -344,6 +345,65 @@ def time_full_vs_active(ada, device, iters: int = 20) -> dict:
     return res
 
 
+def time_rope_step(ada, device, iters: int = 100) -> dict:
+    """The decode step with rotary embedding (VoxCPM #395, section 4: rotate
+    the step's query and key, write the cache rows at position_id, attend over
+    0..position_id) at the MiniCPM shape (batch 4, 32/8 heads, bf16, capacity
+    8192, lockstep positions 4095 and 8191): ada_decode_step_rope against the
+    plain ada_decode_step, and the standalone ada_rope_kv_append, each averaged
+    over back-to-back calls bracketed by HIP events, caches rotated so every
+    call reads HBM."""
+    shp = W.WORKLOADS["minicpm_stream"].shape
+    B, Hq, Hkv, D, S = shp.batch, shp.n_head, shp.n_kv_head, shp.head_dim, shp.capacity
+    R = max(2, math.ceil(2 * MALL_BYTES / kv_bytes(Hkv, D, B * S)))
+    xs = [W.decode_inputs(shp, [S] * B, W.seed_for(3, 40_000 + r), device=device, tail="random") for r in range(R)]
+    k_new, v_new = W.append_inputs(B, Hkv, D, shp.dtype, W.seed_for(3, 41_000), device=device)
+    ws = ada.new_workspace(ada.decode_workspace_bytes(B, Hq, Hkv, D, 256), device)
+    out = torch.empty_like(xs[0]["q"])
+    q_rot = torch.empty_like(xs[0]["q"])
+    scale = 1.0 / math.sqrt(D)
+
+    def timed(fn):
+        fn(0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(SPIN_CYCLES)
+        a.record()
+        for i in range(iters):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / iters
+
+    res = {"workload": "minicpm shape: batch 4, 32/8 heads, head_dim 128, bf16, capacity 8192, lockstep position p",
+           "launches": "decode_step and decode_step_rope: 2 each; rope_kv_append: 1"}
+    for p in (4095, 8191):
+        cos, sin = W.rope_tables([p] * B, D, shp.dtype, device=device)
+        pos_t = torch.full((B,), p, dtype=torch.int32, device=device)
+
+        def plain(i, p=p):
+            x = xs[i % R]
+            ada.decode_step(x["q"], k_new, v_new, x["k_cache"], x["v_cache"], p, scale=scale, out=out, workspace=ws)
+
+        def rope(i, p=p, cos=cos, sin=sin):
+            x = xs[i % R]
+            ada.decode_step_rope(x["q"], k_new, v_new, cos, sin, x["k_cache"], x["v_cache"], p, scale=scale,
+                                 out=out, workspace=ws)
+
+        def append_only(i, cos=cos, sin=sin, pos_t=pos_t):
+            x = xs[i % R]
+            ada.rope_kv_append(x["q"], k_new, v_new, cos, sin, x["k_cache"], x["v_cache"], pos_t, q_out=q_rot)
+
+        nbytes = decode_bytes(B, Hq, Hkv, D, [p + 1] * B)
+        t_plain, t_rope, t_app = timed(plain), timed(rope), timed(append_only)
+        res[f"p{p}"] = {"bytes_per_call": nbytes, "decode_step_us": round(t_plain, 2),
+                        "decode_step_rope_us": round(t_rope, 2), "rope_overhead_us": round(t_rope - t_plain, 2),
+                        "decode_step_rope_GBs": round(nbytes / t_rope / 1e3, 1),
+                        "rope_kv_append_us": round(t_app, 2)}
+    del xs
+    return res
+
+
 def cpu_baseline(seconds: float) -> dict:
     """The fp64 oracle on the same step (three decode calls of the sweep), run
     until ``seconds`` of CPU time have passed (at least one step)."""
@@ -444,6 +504,7 @@ def main(argv=None):
         also["long_context"] = time_long_context(ada, device)
         also["s2pro_run"] = time_s2pro_run(ada, device)
         also["full_capacity_vs_active_prefix"] = time_full_vs_active(ada, device)
+        also["rope_step"] = time_rope_step(ada, device)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
