@@ -27,11 +27,15 @@
 //   * q.k in fp32 with the packed 16-bit dot instructions (products of two
 //     16-bit values are exact in fp32), summed over the L lanes of a row with
 //     DPP butterfly adds; scale*log2(e) is applied to the sum.
-//   * Online softmax in base 2 per lane group (reference max m, sum l, fp32
-//     accumulator), rescaling only when a score exceeds the reference by
-//     more than 2^8 (so almost never after the first rows); lane groups
-//     are merged with DPP and the 16/32-lane permlane swaps, wavefronts
-//     through LDS.
+//   * Online softmax in base 2 with one reference m per head for the whole
+//     wavefront (sum l and fp32 accumulator per lane), rescaling only when a
+//     score exceeds the reference by more than 2^8 (so almost never after
+//     the first rows). At the end the lane groups' sums are added by a
+//     butterfly of 32/16-lane permlane swaps and a DPP rotate that carries
+//     two accumulators per exchange; wavefronts merge through LDS.
+//   * Rotary decode step: the query heads and the new key are rotated once
+//     per workgroup (rotate-half form, correctly rounded to 16 bits) and
+//     shared through LDS ([FORWARD-STEP] section 4).
 //   * With one split the workgroup writes the output directly. With several
 //     splits each workgroup stores its (m, l, acc) partial and a second,
 //     small kernel merges a row's partials in split order (log-sum-exp
