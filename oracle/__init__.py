@@ -96,6 +96,11 @@ class Oracle:
         lib.ada_oracle_f16_to_f64.restype = ctypes.c_double
         lib.ada_oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
         lib.ada_oracle_bf16_to_f64.restype = ctypes.c_double
+        lib.ada_oracle_prefill.argtypes = [u16p, u16p, u16p, i32p, c_int, c_int, c_int, c_int, c_int, c_int,
+                                           ctypes.c_double, c_int, f64p]
+        lib.ada_oracle_prefill.restype = c_int
+        lib.ada_oracle_prefill_append.argtypes = [u16p, u16p, u16p, u16p, i32p, c_int, c_int, c_int, c_int, c_int]
+        lib.ada_oracle_prefill_append.restype = c_int
         lib.ada_oracle_threads.argtypes = []
         lib.ada_oracle_threads.restype = c_int
         self._lib = lib
@@ -129,6 +134,45 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle decode failed with status {rc}")
         return out
+
+    def prefill(self, q, k_cache, v_cache, start, scale: float, dtype: str | None = None) -> np.ndarray:
+        """Causal prefill: out[b, h, t, :] in float64 for q [B, Hq, T, D], caches
+        [B, Hkv, S, D]; token t of row b attends slots 0 .. start[b] + t."""
+        dt = _dtype_name(q, dtype)
+        qb, kb, vb = _bits(q), _bits(k_cache), _bits(v_cache)
+        batch, n_head, q_len, head_dim = qb.shape
+        kb_, n_kv_head, capacity, kd = kb.shape
+        if kb.shape != vb.shape or kb_ != batch or kd != head_dim:
+            raise ValueError("inconsistent shapes")
+        st = np.ascontiguousarray(np.asarray(
+            start.cpu().numpy() if hasattr(start, "cpu") else start, dtype=np.int32).reshape(batch))
+        out = np.zeros((batch, n_head, q_len, head_dim), dtype=np.float64)
+        rc = self._lib.ada_oracle_prefill(_ptr(qb, ctypes.c_uint16), _ptr(kb, ctypes.c_uint16),
+                                          _ptr(vb, ctypes.c_uint16), _ptr(st, ctypes.c_int32), batch, n_head,
+                                          n_kv_head, q_len, head_dim, capacity, float(scale), DTYPES[dt],
+                                          _ptr(out, ctypes.c_double))
+        if rc != 0:
+            raise ValueError(f"oracle prefill failed with status {rc}")
+        return out
+
+    def prefill_append(self, k_new, v_new, k_cache, v_cache, start):
+        """Return updated copies of the caches with the T new rows [B, Hkv, T, D]
+        written at slots start[b] .. start[b] + T - 1 (inputs not modified)."""
+        kn, vn = np.ascontiguousarray(_bits(k_new)), np.ascontiguousarray(_bits(v_new))
+        kc, vc = _bits(k_cache).copy(), _bits(v_cache).copy()
+        batch, n_kv_head, capacity, head_dim = kc.shape
+        q_len = kn.shape[2]
+        if kn.shape != (batch, n_kv_head, q_len, head_dim) or vn.shape != kn.shape:
+            raise ValueError("k_new / v_new must be [B, Hkv, T, D]")
+        st = np.ascontiguousarray(np.asarray(
+            start.cpu().numpy() if hasattr(start, "cpu") else start, dtype=np.int32).reshape(batch))
+        rc = self._lib.ada_oracle_prefill_append(_ptr(kn, ctypes.c_uint16), _ptr(vn, ctypes.c_uint16),
+                                                 _ptr(kc, ctypes.c_uint16), _ptr(vc, ctypes.c_uint16),
+                                                 _ptr(st, ctypes.c_int32), batch, n_kv_head, q_len, capacity,
+                                                 head_dim)
+        if rc != 0:
+            raise ValueError(f"oracle prefill_append failed with status {rc}")
+        return kc, vc
 
     def kv_append(self, k_new, v_new, k_cache, v_cache, pos):
         """Return updated copies of the caches (inputs are not modified)."""

@@ -219,3 +219,130 @@ int ada_oracle_kv_append(const uint16_t* k_new, const uint16_t* v_new,
   }
   return 0;
 }
+
+/*
+ * Causal prefill attention over the cache: T query tokens per batch row at
+ * positions start[b] .. start[b] + T - 1, each attending to every cache slot
+ * up to and including its own position. The prompt's keys and values are
+ * already in the cache (ada_oracle_prefill_append below).
+ *
+ *   q        [batch, n_head, T, head_dim]     16-bit values (the head-major
+ *                                             query of an SDPA call)
+ *   k_cache, v_cache [batch, n_kv_head, capacity, head_dim]
+ *   start    [batch]  position of the first query token of each row
+ *   out      [batch, n_head, T, head_dim]     double, unrounded
+ *
+ * The pages run prompt prefill as SDPA with is_causal=True over the prompt
+ * ([FORWARD-STEP] section 5, forward() keeps is_causal=True), with the cache
+ * holding kv_len = T slots after it ([ACTIVE-PREFIX] section 2). Query token
+ * t of batch row b, head h (KV head g = h / G as in the decode):
+ *   n = clamp(start[b] + t + 1, 0, capacity)
+ *   x_j = scale * sum_d q[b,h,t,d] * K[b,g,j,d]      for j < n
+ *   out[b,h,t,:] = sum_j exp(x_j - m) V[b,g,j,:] / sum_j exp(x_j - m),  m = max_j x_j
+ * With start = 0 this is the causal (lower-triangular) mask of a square
+ * score matrix; with start > 0 (a prompt continued after earlier tokens) each
+ * token still sees exactly the slots up to its own position. n == 0 gives a
+ * zero row.
+ */
+int ada_oracle_prefill(const uint16_t* q, const uint16_t* k_cache,
+                       const uint16_t* v_cache, const int32_t* start,
+                       int batch, int n_head, int n_kv_head, int q_len,
+                       int head_dim, int capacity, double scale, int dtype,
+                       double* out) {
+  if (batch < 0 || n_head <= 0 || n_kv_head <= 0 || q_len < 0 ||
+      head_dim <= 0 || capacity <= 0 || n_head % n_kv_head != 0 ||
+      (dtype != ORACLE_F16 && dtype != ORACLE_BF16))
+    return -1;
+  if (batch == 0 || q_len == 0) return 0;
+  if (!q || !k_cache || !v_cache || !start || !out) return -1;
+
+  const int group = n_head / n_kv_head;
+  const long rows = (long)batch * n_head * q_len;
+  int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+  for (long r = 0; r < rows; ++r) {
+    const int t = (int)(r % q_len);
+    const int h = (int)((r / q_len) % n_head);
+    const int b = (int)(r / ((long)q_len * n_head));
+    const int g = h / group;
+    long nl = (long)start[b] + t + 1;
+    if (nl < 0) nl = 0;
+    if (nl > capacity) nl = capacity;
+    const int n = (int)nl;
+
+    double* o = out + r * head_dim;
+    for (int d = 0; d < head_dim; ++d) o[d] = 0.0;
+    if (n == 0) continue;
+
+    const uint16_t* qrow = q + r * head_dim;
+    const uint16_t* kbase =
+        k_cache + ((size_t)b * n_kv_head + g) * (size_t)capacity * head_dim;
+    const uint16_t* vbase =
+        v_cache + ((size_t)b * n_kv_head + g) * (size_t)capacity * head_dim;
+
+    double* qd = (double*)malloc(sizeof(double) * head_dim);
+    double* x = (double*)malloc(sizeof(double) * n);
+    if (!qd || !x) {
+      free(qd);
+      free(x);
+      failed = 1;
+      continue;
+    }
+    for (int d = 0; d < head_dim; ++d) qd[d] = decode16(qrow[d], dtype);
+    for (int j = 0; j < n; ++j) {
+      const uint16_t* krow = kbase + (size_t)j * head_dim;
+      double dot = 0.0;
+      for (int d = 0; d < head_dim; ++d) dot += qd[d] * decode16(krow[d], dtype);
+      x[j] = scale * dot;
+    }
+    double m = x[0];
+    for (int j = 1; j < n; ++j)
+      if (x[j] > m) m = x[j];
+    double wsum = 0.0;
+    for (int j = 0; j < n; ++j) {
+      x[j] = exp(x[j] - m);
+      wsum += x[j];
+    }
+    for (int j = 0; j < n; ++j) {
+      const uint16_t* vrow = vbase + (size_t)j * head_dim;
+      for (int d = 0; d < head_dim; ++d) o[d] += x[j] * decode16(vrow[d], dtype);
+    }
+    for (int d = 0; d < head_dim; ++d) o[d] /= wsum;
+    free(qd);
+    free(x);
+  }
+  return failed ? -2 : 0;
+}
+
+/*
+ * Prompt append: the T new key and value rows of every (batch row, KV head)
+ * go to slots start[b] .. start[b] + T - 1 of the preallocated caches, bit
+ * for bit ([ACTIVE-PREFIX] section 2: prefill fills the first kv_len = T
+ * slots, the allocation is unchanged). Rows whose slot falls outside
+ * [0, capacity) are not written.
+ *
+ *   k_new, v_new [batch, n_kv_head, T, head_dim]
+ */
+int ada_oracle_prefill_append(const uint16_t* k_new, const uint16_t* v_new,
+                              uint16_t* k_cache, uint16_t* v_cache,
+                              const int32_t* start, int batch, int n_kv_head,
+                              int q_len, int capacity, int head_dim) {
+  if (batch < 0 || n_kv_head <= 0 || q_len < 0 || capacity <= 0 || head_dim <= 0)
+    return -1;
+  if (batch == 0 || q_len == 0) return 0;
+  if (!k_new || !v_new || !k_cache || !v_cache || !start) return -1;
+  for (int b = 0; b < batch; ++b) {
+    for (int g = 0; g < n_kv_head; ++g) {
+      for (int t = 0; t < q_len; ++t) {
+        long p = (long)start[b] + t;
+        if (p < 0 || p >= capacity) continue;
+        size_t src = (((size_t)b * n_kv_head + g) * q_len + t) * head_dim;
+        size_t dst = (((size_t)b * n_kv_head + g) * capacity + (size_t)p) * head_dim;
+        memcpy(k_cache + dst, k_new + src, sizeof(uint16_t) * head_dim);
+        memcpy(v_cache + dst, v_new + src, sizeof(uint16_t) * head_dim);
+      }
+    }
+  }
+  return 0;
+}

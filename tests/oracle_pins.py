@@ -377,4 +377,84 @@ def pin_append_then_decode_is_forward_step(o):
     _close(got, want, 1e-12, "append then decode")
 
 
+# ---------------------------------------------------------------------------
+# Prefill: T query tokens per row at positions start[b] + t, causal.
+
+
+def _prefill_inputs(B, Hq, Hkv, D, S, T, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    dt = W.TORCH_DTYPES[dtype]
+    q = torch.randn((B, Hq, T, D), generator=g).to(dt)
+    k = torch.randn((B, Hkv, S, D), generator=g).to(dt)
+    v = torch.randn((B, Hkv, S, D), generator=g).to(dt)
+    return q, k, v
+
+
+def pin_prefill_matches_library_causal_sdpa(o):
+    """Prompt prefill from slot 0 is SDPA with is_causal=True over the T prompt
+    slots ([FORWARD-STEP] section 5: the batch prefill path keeps is_causal;
+    [ACTIVE-PREFIX] section 2: kv_len = T after prefill), float64 on the CPU."""
+    for (B, Hq, Hkv, D, T, dtype) in ((1, 4, 1, 16, 9, "fp16"), (2, 8, 2, 32, 17, "bf16"), (1, 32, 8, 128, 33, "fp16")):
+        S = T + 5  # slots past the prompt hold values that must not be seen
+        q, k, v = _prefill_inputs(B, Hq, Hkv, D, S, T, dtype, 600 + T)
+        k[:, :, T:] = float("nan")
+        v[:, :, T:] = float("nan")
+        scale = 1.0 / math.sqrt(D)
+        got = o.prefill(q, k, v, [0] * B, scale)
+        want = F.scaled_dot_product_attention(_f64(q), _f64(k[:, :, :T]).contiguous(), _f64(v[:, :, :T]).contiguous(),
+                                              is_causal=True, scale=scale, enable_gqa=True).numpy()
+        _close(got, want, 1e-12, f"prefill vs causal SDPA {B}x{Hq}/{Hkv}x{T}x{D}")
+
+
+def pin_prefill_continued_prompt_mask(o):
+    """A prompt continued at start > 0: token t sees slots 0 .. start + t, the
+    boolean mask j <= start + t over the first start + T slots (SDPA with an
+    explicit mask; different rows, different starts)."""
+    B, Hq, Hkv, D, S, T = 3, 8, 2, 32, 64, 7
+    q, k, v = _prefill_inputs(B, Hq, Hkv, D, S, T, "bf16", 610)
+    starts = [0, 10, 57]
+    scale = 0.17
+    got = o.prefill(q, k, v, starts, scale)
+    for b, st in enumerate(starts):
+        n = st + T
+        mask = torch.arange(n)[None, :] <= (st + torch.arange(T))[:, None]
+        want = F.scaled_dot_product_attention(_f64(q[b:b + 1]), _f64(k[b:b + 1, :, :n]).contiguous(),
+                                              _f64(v[b:b + 1, :, :n]).contiguous(), attn_mask=mask, scale=scale,
+                                              enable_gqa=True).numpy()
+        _close(got[b:b + 1], want, 1e-12, f"continued prompt start={st}")
+
+
+def pin_prefill_rows_are_decode_calls(o):
+    """Each prefill token is a single-token decode over kv_len = start + t + 1
+    (and the slots past a clamped position are the whole cache)."""
+    B, Hq, Hkv, D, S, T = 2, 6, 3, 8, 20, 6
+    q, k, v = _prefill_inputs(B, Hq, Hkv, D, S, T, "fp16", 620)
+    starts = [3, 17]  # the second row runs past the cache: clamped to S slots
+    got = o.prefill(q, k, v, starts, 0.3)
+    for t in range(T):
+        lens = [min(S, st + t + 1) for st in starts]
+        want = _sdpa_reference(q[:, :, t, :], k, v, lens, 0.3)
+        _close(got[:, :, t, :], want, 1e-12, f"prefill token {t}")
+
+
+def pin_prefill_append_matches_slice_assign(o):
+    """The prompt's rows land at slots start .. start + T - 1, bit for bit;
+    rows outside the cache are dropped; nothing else changes."""
+    B, Hkv, D, S, T = 3, 2, 8, 16, 5
+    g = torch.Generator().manual_seed(630)
+    kc = torch.randn((B, Hkv, S, D), generator=g).to(torch.float16)
+    vc = torch.randn((B, Hkv, S, D), generator=g).to(torch.float16)
+    kn = torch.randn((B, Hkv, T, D), generator=g).to(torch.float16)
+    vn = torch.randn((B, Hkv, T, D), generator=g).to(torch.float16)
+    starts = [0, 9, 13]
+    got_k, got_v = o.prefill_append(kn, vn, kc, vc, starts)
+    want_k, want_v = kc.clone(), vc.clone()
+    for b, st in enumerate(starts):
+        m = min(T, S - st)
+        want_k[b, :, st:st + m] = kn[b, :, :m]
+        want_v[b, :, st:st + m] = vn[b, :, :m]
+    to_bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got_k, to_bits(want_k)) and np.array_equal(got_v, to_bits(want_v)), "prefill append"
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -52,6 +52,20 @@ MUTANTS = [
     # append writes slot pos + 1
     ("append_off_by_one", "(((size_t)b * n_kv_head + g) * capacity + p) * head_dim",
      "(((size_t)b * n_kv_head + g) * capacity + p + (p + 1 < capacity)) * head_dim"),
+    # prefill: a token sees only the slots before its own position
+    ("prefill_off_by_one", "long nl = (long)start[b] + t + 1;", "long nl = (long)start[b] + t;"),
+    # prefill: the prompt's first position ignored (top-left causal alignment)
+    ("prefill_ignores_start", "long nl = (long)start[b] + t + 1;", "long nl = (long)t + 1;"),
+    # prefill: token-major instead of head-major query layout
+    ("prefill_query_layout", "const int t = (int)(r % q_len);\n    const int h = (int)((r / q_len) % n_head);",
+     "const int h = (int)(r % n_head);\n    const int t = (int)((r / n_head) % q_len);"),
+    # prefill: tile head map
+    ("prefill_head_map", "const int g = h / group;\n    long nl", "const int g = h % n_kv_head;\n    long nl"),
+    # prefill append: rows written one slot late
+    ("prefill_append_shift", "long p = (long)start[b] + t;", "long p = (long)start[b] + t + 1;"),
+    # prefill append: source row of the wrong token
+    ("prefill_append_source", "size_t src = (((size_t)b * n_kv_head + g) * q_len + t) * head_dim;",
+     "size_t src = (((size_t)b * n_kv_head + g) * q_len) * head_dim;"),
     # append ignores the out-of-range guard on the low side (writes slot 0)
     ("append_negative_pos", "if (p < 0 || p >= capacity) continue;",
      "if (p >= capacity) continue;\n    if (p < 0) p = 0;"),
