@@ -46,7 +46,8 @@ EXPORTS = (
     "ada_abi_version", "ada_status_string", "ada_last_hip_error", "ada_device_num_cus",
     "ada_kv_append", "ada_decode_num_splits", "ada_decode_workspace_bytes",
     "ada_decode_attn_gqa", "ada_decode_attn_gqa_ex", "ada_decode_partial", "ada_decode_combine",
-    "ada_decode_step", "ada_rope_kv_append", "ada_decode_step_rope",
+    "ada_decode_step", "ada_rope_kv_append", "ada_decode_step_rope", "ada_prefill_append",
+    "ada_prefill_attn_gqa",
 )
 
 
@@ -83,6 +84,8 @@ def _declare(lib):
         "ada_decode_step": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                              c_int, c_int, c_float, c_int, c_void_p, c_void_p, c_size_t, c_void_p, c_int], c_int),
         "ada_rope_kv_append": ([c_void_p] * 9 + [c_int] * 6 + [c_void_p], c_int),
+        "ada_prefill_append": ([c_void_p] * 5 + [c_int] * 6 + [c_void_p], c_int),
+        "ada_prefill_attn_gqa": ([c_void_p] * 4 + [c_int] * 6 + [c_float, c_int, c_void_p, c_void_p], c_int),
         "ada_decode_step_rope": ([c_void_p] * 8 + [c_int] * 6 + [c_float, c_int, c_void_p, c_void_p, c_size_t,
                                                                  c_void_p, c_int], c_int),
     }
@@ -400,6 +403,62 @@ def rope_kv_append(q, k_new: torch.Tensor, v_new: torch.Tensor, cos: torch.Tenso
     return q_out
 
 
+def _start_arg(start, batch: int, device):
+    """None or 0 -> NULL (every row from slot 0); else an int32 device tensor."""
+    if start is None or (not isinstance(start, torch.Tensor) and not hasattr(start, "__len__") and int(start) == 0):
+        return None
+    if not isinstance(start, torch.Tensor) and not hasattr(start, "__len__"):
+        start = [int(start)] * batch
+    return _as_int32(start, batch, device)
+
+
+def prefill_append(k_new: torch.Tensor, v_new: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   start=None) -> None:
+    """Write the prompt rows k_new/v_new [B, Hkv, T, D] into slots start[b] ..
+    start[b] + T - 1 of the caches [B, Hkv, S, D], in place. ``start``: None
+    (slot 0), a host int or ints, or an int32 GPU tensor [B]."""
+    _require(k_cache.is_cuda and k_cache.dim() == 4, "k_cache must be a 4-d GPU tensor [B, Hkv, S, D]")
+    B, Hkv, S, D = k_cache.shape
+    _require(v_cache.shape == k_cache.shape, "v_cache shape must equal k_cache shape")
+    _require(k_cache.dtype in _DTYPE_CODES, "dtype must be float16 or bfloat16")
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _require(t.dtype == k_cache.dtype and t.device == k_cache.device and t.is_contiguous(),
+                 f"{name} must be contiguous, on {k_cache.device}, dtype {k_cache.dtype}")
+    _require(k_new.dim() == 4 and k_new.shape[:2] == (B, Hkv) and k_new.shape[3] == D and v_new.shape == k_new.shape,
+             "k_new/v_new must be [B, Hkv, T, D]")
+    T = k_new.shape[2]
+    st = _start_arg(start, B, k_cache.device)
+    _check(_lib.ada_prefill_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(st), B, Hkv, T, S, D,
+                                   _DTYPE_CODES[k_cache.dtype], ctypes.c_void_p(_stream(k_cache.device))),
+           "ada_prefill_append")
+
+
+def prefill_attn_gqa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, start=None,
+                     scale: float | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Causal prefill attention: q [B, Hq, T, D]; token t of row b attends cache
+    slots 0 .. start[b] + t (start None = 0: SDPA with is_causal=True over the
+    prompt). Returns out [B, Hq, T, D]."""
+    _require(q.is_cuda and q.dim() == 4, "q must be a 4-d GPU tensor [B, Hq, T, D]")
+    _require(k_cache.dim() == 4 and v_cache.shape == k_cache.shape, "caches must be [B, Hkv, S, D]")
+    B, Hq, T, D = q.shape
+    _, Hkv, S, _ = k_cache.shape
+    _require(k_cache.shape[0] == B and k_cache.shape[3] == D, "q and caches disagree")
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache)):
+        _require(t.dtype == q.dtype and t.device == q.device and t.is_contiguous(),
+                 f"{name} must be contiguous, on {q.device}, dtype {q.dtype}")
+    _require(q.dtype in _DTYPE_CODES, "dtype must be float16 or bfloat16")
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous(), "out must be like q")
+    st = _start_arg(start, B, q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(_lib.ada_prefill_attn_gqa(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(st), B, Hq, Hkv, T, D, S,
+                                     ctypes.c_float(scale), _DTYPE_CODES[q.dtype], _ptr(out),
+                                     ctypes.c_void_p(_stream(q.device))),
+           "ada_prefill_attn_gqa")
+    return out
+
+
 def _decode_step(q, k_new, v_new, cos, sin, k_cache, v_cache, pos, scale, out, max_pos, num_splits, workspace):
     B, Hq, Hkv, S, D = _check_decode_inputs(q, k_cache, v_cache)
     if cos is not None or sin is not None:
@@ -461,7 +520,7 @@ def decode_attn_gqa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
 __all__ = [
     "AdaError", "F16", "BF16", "HEAD_DIM", "MAX_SPLITS", "EXPORTS", "LIB_PATH", "load_library",
     "kv_append", "decode_attn_gqa", "decode_attn_gqa_ex", "decode_partial", "decode_combine", "decode_step", "decode_step_rope",
-    "rope_kv_append", "decode_num_splits", "decode_workspace_bytes",
+    "rope_kv_append", "prefill_append", "prefill_attn_gqa", "decode_num_splits", "decode_workspace_bytes",
     "new_workspace", "workspace_layout", "device_num_cus", "status_string", "last_hip_error",
     "abi_version",
 ]

@@ -344,6 +344,53 @@ int ada_decode_step_rope(const void* q, const void* k_new, const void* v_new, co
                           capacity, max_pos, scale, dtype, out, workspace, workspace_bytes, stream, num_splits);
 }
 
+int ada_prefill_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache, const int32_t* start,
+                       int batch, int n_kv_head, int q_len, int capacity, int head_dim, int dtype, void* stream) {
+  if (dtype != ADA_F16 && dtype != ADA_BF16) return ADA_ERR_DTYPE;
+  if (batch < 0 || n_kv_head <= 0 || q_len < 0 || capacity <= 0) return ADA_ERR_SHAPE;
+  if (head_dim != ada::kHeadDim) return ADA_ERR_HEAD_DIM;
+  const int64_t chunks = static_cast<int64_t>(batch) * n_kv_head * q_len * (ada::kHeadDim * 2 / 16);
+  if ((chunks + 255) / 256 > INT32_MAX) return ADA_ERR_SHAPE;
+  if (batch == 0 || q_len == 0) return ADA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache) return ADA_ERR_NULL;  // start may be NULL (slot 0)
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache)) return ADA_ERR_ALIGN;
+  hipError_t e = ada::launch_prefill_append(k_new, v_new, k_cache, v_cache, start, batch, n_kv_head, q_len, capacity,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ADA_OK : hip_fail(e);
+}
+
+int ada_prefill_attn_gqa(const void* q, const void* k_cache, const void* v_cache, const int32_t* start, int batch,
+                         int n_head, int n_kv_head, int q_len, int head_dim, int capacity, float scale, int dtype,
+                         void* out, void* stream) {
+  if (dtype != ADA_F16 && dtype != ADA_BF16) return ADA_ERR_DTYPE;
+  if (batch < 0 || n_head <= 0 || n_kv_head <= 0 || q_len < 0 || capacity <= 0) return ADA_ERR_SHAPE;
+  if (n_head % n_kv_head != 0 || n_head / n_kv_head > ada::kMaxGroup) return ADA_ERR_GQA;
+  if (head_dim != ada::kHeadDim) return ADA_ERR_HEAD_DIM;
+  if (!std::isfinite(scale)) return ADA_ERR_SCALE;
+  const int64_t row_tiles = ceil_div(static_cast<int64_t>(n_head / n_kv_head) * q_len, 64);
+  if (row_tiles * batch * n_kv_head > INT32_MAX) return ADA_ERR_SHAPE;
+  if (static_cast<int64_t>(batch) * n_head * q_len * head_dim > (int64_t(1) << 40)) return ADA_ERR_SHAPE;
+  if (batch == 0 || q_len == 0) return ADA_OK;
+  if (!q || !k_cache || !v_cache || !out) return ADA_ERR_NULL;  // start may be NULL (slot 0)
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return ADA_ERR_ALIGN;
+  ada::PrefillLaunch p{};
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.start = start;
+  p.out = out;
+  p.batch = batch;
+  p.n_head = n_head;
+  p.n_kv_head = n_kv_head;
+  p.q_len = q_len;
+  p.capacity = capacity;
+  p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  p.dtype = dtype;
+  p.stream = static_cast<hipStream_t>(stream);
+  hipError_t e = ada::launch_prefill(p);
+  return e == hipSuccess ? ADA_OK : hip_fail(e);
+}
+
 int ada_decode_partial(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* kv_len, int batch, int n_head, int n_kv_head, int head_dim,
                        int capacity, int max_kv_len, float scale, int dtype, int num_splits,

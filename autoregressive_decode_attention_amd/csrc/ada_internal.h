@@ -58,6 +58,23 @@ struct CombineLaunch {
   hipStream_t stream;
 };
 
+struct PrefillLaunch {
+  const void* q;        // [B, H_q, T, D]
+  const void* k_cache;  // [B, H_kv, S, D]
+  const void* v_cache;
+  const int32_t* start;  // device [B] first position of each row, or NULL (0)
+  void* out;             // [B, H_q, T, D]
+  int batch, n_head, n_kv_head, q_len, capacity;
+  float scale_log2;
+  int dtype;
+  hipStream_t stream;
+};
+
+hipError_t launch_prefill(const PrefillLaunch& p);
+hipError_t launch_prefill_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                 const int32_t* start, int batch, int n_kv_head, int q_len, int capacity,
+                                 hipStream_t stream);
+
 hipError_t launch_partial(const DecodeLaunch& p);
 hipError_t launch_combine(const CombineLaunch& p);
 

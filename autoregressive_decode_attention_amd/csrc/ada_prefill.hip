@@ -1,0 +1,365 @@
+// ada_prefill.hip -- gfx950 kernels of libada for prompt prefill: the T
+// prompt rows appended to the preallocated cache, and causal attention of the
+// T prompt tokens over the cache.
+//
+// Pages cited (by title and section):
+//   [ACTIVE-PREFIX] fish-speech issue #1310, "Optimize native AR decoding by
+//                   attending only to the active KV-cache prefix" (section 2:
+//                   kv_len = T after the prompt prefill).
+//   [FORWARD-STEP]  VoxCPM issue #395, "MiniCPM4 MiniCPMAttention.forward_step
+//                   Attention Performance Fix" (section 5: the batch prefill
+//                   path runs attention with is_causal=True).
+//
+// Token t of batch row b sits at position start[b] + t and attends cache
+// slots 0 .. start[b] + t (start = 0: the square causal mask of a prompt).
+// Unlike the one-token decode, this is a dense contraction: G*T query rows
+// share every key and value row of their KV head, so the scores and the
+// weighted sum of values run on the matrix cores.
+//
+// Attention kernel, per workgroup: one (batch row, KV head) and 64 query
+// rows, where row r of the head group is token r / G and query head
+// g*G + r % G (the G heads of a token share its causal limit). Four
+// wavefronts own 16 rows each. Key/value tiles of 64 slots go through LDS:
+//   * S^T = K Q^T with v_mfma_f32_16x16x32 (16-bit inputs, fp32 sums): keys
+//     on M, query rows on N, head dims on K. A lane then holds, for one query
+//     row, 16 scores (4 keys in each of the tile's four 16-key blocks).
+//   * Online softmax in base 2 per row in fp32, exact running maximum; the
+//     weights are rounded once to the 16-bit type and the row sums use the
+//     rounded weights, so numerator and denominator see the same values.
+//   * O += P V with the same instruction: P is the A operand straight from
+//     registers, its K index running over the lane's 8 keys of a 32-key step
+//     (a fixed permutation of the keys, the same one the V operand uses).
+//     V is stored transposed in LDS ([dim][key]) so that each lane reads its
+//     8 keys of one dim as two 8-byte loads.
+//   * Row statistics move from the score layout (row = lane % 16) to the
+//     output layout (rows 4 * (lane / 16) + j) with ds_bpermute.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ada_internal.h"
+
+namespace ada {
+namespace {
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+struct PF16 {
+  static __device__ __forceinline__ f4 mma(const uint4& a, const uint4& b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t round(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  }
+  static __device__ __forceinline__ float to_float(uint32_t bits) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+  }
+};
+
+struct PBF16 {
+  static __device__ __forceinline__ f4 mma(const uint4& a, const uint4& b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t round(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+  }
+  static __device__ __forceinline__ float to_float(uint32_t bits) { return __uint_as_float(bits << 16); }
+};
+
+constexpr int D = kHeadDim;     // 128
+constexpr int kRowsWG = 64;      // query rows per workgroup
+constexpr int kKeys = 64;        // key/value slots per tile
+constexpr int kKStride = D + 8;  // K tile row stride in LDS (u16): 272 B, 4-bank rotation per row
+constexpr int kVStride = 68;     // transposed V row stride (u16): 34 dwords, 2-bank rotation per row
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ float finite_ref(float m) { return m == kNegInf ? 0.0f : m; }
+
+__device__ __forceinline__ float xor16_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Value of x held by lane `src` of the wavefront.
+__device__ __forceinline__ float from_lane(float x, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+}
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Number of cache slots token t of a row starting at `start` attends to.
+__device__ __forceinline__ int visible(int start, int t, int capacity) {
+  const long n = static_cast<long>(start) + t + 1;
+  return n < 0 ? 0 : (n > capacity ? capacity : static_cast<int>(n));
+}
+
+template <class E, int G>
+__global__ __launch_bounds__(256) void prefill_kernel(const uint16_t* __restrict__ q,
+                                                      const uint16_t* __restrict__ k_cache,
+                                                      const uint16_t* __restrict__ v_cache,
+                                                      const int32_t* __restrict__ start_arr,
+                                                      uint16_t* __restrict__ out, int n_kv_head, int q_len,
+                                                      int capacity, int units, int row_tiles, float scale_log2) {
+  __shared__ __align__(16) uint16_t s_k[kKeys * kKStride];
+  __shared__ __align__(16) uint16_t s_vt[D * kVStride];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int a = lane >> 4;     // 16-lane group
+  const int lr = lane & 15;    // lane within the group
+  // Workgroups of the same (batch row, KV head) are `units` apart; the
+  // longest row tiles (latest tokens, most keys) launch first.
+  const int unit = blockIdx.x % units;
+  const int rt = row_tiles - 1 - blockIdx.x / units;
+  const int b = unit / n_kv_head;
+  const int g = unit % n_kv_head;
+  const int n_head = n_kv_head * G;
+  const int rows = G * q_len;
+  const int start = start_arr != nullptr ? start_arr[b] : 0;
+  const int r0 = rt * kRowsWG;
+  const int t_last = min(q_len - 1, (min(r0 + kRowsWG, rows) - 1) / G);
+  const int n_max = visible(start, t_last, capacity);
+  const int ntiles = (n_max + kKeys - 1) / kKeys;
+
+  const size_t head_off = static_cast<size_t>(unit) * capacity * D;
+  const uint16_t* kbase = k_cache + head_off;
+  const uint16_t* vbase = v_cache + head_off;
+
+  // This lane's query row in the score layout (row lr of the wave's 16).
+  const int my_row = r0 + wave * 16 + lr;
+  const int my_t = my_row / G;
+  const bool row_ok = my_row < rows;
+  const int my_n = row_ok ? visible(start, my_t, capacity) : 0;
+  uint4 qb[4];  // Q^T operand: dims 32*ks + 8*a .. + 8 of row my_row
+  {
+    const int i = my_row % G;
+    const uint16_t* qrow = q + ((static_cast<size_t>(b) * n_head + g * G + i) * q_len + (row_ok ? my_t : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[ks] = row_ok ? ld16(qrow + 32 * ks + 8 * a) : make_uint4(0, 0, 0, 0);
+  }
+
+  f4 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = kNegInf;  // running max of row my_row (same in its 4 lanes)
+  float l_run = 0.0f;     // this lane's share of the row's weight sum
+
+  // Tile staging: K as 4 row chunks per thread (16 threads per 256-byte row),
+  // V as two rows x one 16-byte chunk (key pair kp, dims 8c .. 8c + 8) twice.
+  uint4 kreg[4], vreg[2][2];
+  auto load_tile = [&](int tile) {
+    const int base = tile * kKeys;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = tid + 256 * it;
+      const int key = min(base + idx / 16, n_max - 1);
+      kreg[it] = ld16(kbase + static_cast<size_t>(key) * D + 8 * (idx % 16));
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int kp = tid % 32;
+      const int c = tid / 32 + 8 * it;
+      const int k0 = min(base + 2 * kp, n_max - 1);
+      const int k1 = min(base + 2 * kp + 1, n_max - 1);
+      vreg[it][0] = ld16(vbase + static_cast<size_t>(k0) * D + 8 * c);
+      vreg[it][1] = ld16(vbase + static_cast<size_t>(k1) * D + 8 * c);
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = tid + 256 * it;
+      *reinterpret_cast<uint4*>(s_k + (idx / 16) * kKStride + 8 * (idx % 16)) = kreg[it];
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int kp = tid % 32;
+      const int c = tid / 32 + 8 * it;
+      const uint32_t* r0w = reinterpret_cast<const uint32_t*>(&vreg[it][0]);
+      const uint32_t* r1w = reinterpret_cast<const uint32_t*>(&vreg[it][1]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // dims 8c + 2w (low halves) and 8c + 2w + 1 (high halves) of keys 2kp, 2kp + 1
+        const uint32_t lo = (r0w[w] & 0xffffu) | (r1w[w] << 16);
+        const uint32_t hi = (r0w[w] >> 16) | (r1w[w] & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(s_vt + (8 * c + 2 * w) * kVStride + 2 * kp) = lo;
+        *reinterpret_cast<uint32_t*>(s_vt + (8 * c + 2 * w + 1) * kVStride + 2 * kp) = hi;
+      }
+    }
+  };
+
+  if (ntiles > 0) load_tile(0);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    __syncthreads();  // every wave is done with the previous tile
+    store_tile();
+    __syncthreads();
+    if (tile + 1 < ntiles) load_tile(tile + 1);
+    const int base = tile * kKeys;
+
+    // S^T = K Q^T: block nb holds keys base + 16*nb + 4*a + j for row my_row.
+    f4 s[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      s[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 kop = *reinterpret_cast<const uint4*>(s_k + (16 * nb + lr) * kKStride + 32 * ks + 8 * a);
+        s[nb] = E::mma(kop, qb[ks], s[nb]);
+      }
+    }
+    // Scale, mask (slots past the row's own position), tile maximum.
+    float x[4][4];
+    float mx = kNegInf;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = base + 16 * nb + 4 * a + j;
+        x[nb][j] = key < my_n ? s[nb][j] * scale_log2 : kNegInf;
+        mx = fmaxf(mx, x[nb][j]);
+      }
+    }
+    mx = xor32_max(xor16_max(mx));  // over the row's 4 lanes
+    const float m_new = fmaxf(m_run, mx);
+    const float ref = finite_ref(m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - ref);  // 0 while nothing was seen
+    m_run = m_new;
+    l_run *= alpha;
+    // Weights, rounded to the 16-bit type, packed as the A operand of P V:
+    // step ks2 holds keys base + 32*ks2 + 4*a + j (first half) and
+    // base + 32*ks2 + 16 + 4*a + j (second half), j = 0..3.
+    uint4 pa[2];
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int nb = 2 * ks2 + h;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const uint32_t p0 = E::round(__builtin_amdgcn_exp2f(x[nb][2 * jj] - ref));
+          const uint32_t p1 = E::round(__builtin_amdgcn_exp2f(x[nb][2 * jj + 1] - ref));
+          l_run += E::to_float(p0) + E::to_float(p1);
+          w[2 * h + jj] = p0 | (p1 << 16);
+        }
+      }
+      pa[ks2] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    // Rescale the output rows this lane holds (rows 4*a + j of the wave).
+    float al[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) al[j] = from_lane(alpha, 4 * a + j);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[db][j] *= al[j];
+    }
+    // O += P V: B operand = V at the same 8 keys, dim 16*db + lr.
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const uint16_t* vrow = s_vt + (16 * db + lr) * kVStride + 32 * ks2 + 4 * a;
+        const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
+        const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
+        o[db] = E::mma(pa[ks2], make_uint4(v0.x, v0.y, v1.x, v1.y), o[db]);
+      }
+    }
+  }
+
+  // Normalise and store: lane holds rows 4*a + j, dims 16*db + lr.
+  const float l_row = xor32_sum(xor16_sum(l_run));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lj = from_lane(l_row, 4 * a + j);
+    const int row = r0 + wave * 16 + 4 * a + j;
+    if (row >= rows) continue;
+    const int t = row / G;
+    const int i = row % G;
+    uint16_t* orow = out + ((static_cast<size_t>(b) * n_head + g * G + i) * q_len + t) * D;
+    const float inv = lj > 0.0f ? 1.0f / lj : 0.0f;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) orow[16 * db + lr] = static_cast<uint16_t>(E::round(o[db][j] * inv));
+  }
+}
+
+// Prompt append: row t of every (batch row, KV head) to slot start[b] + t,
+// as 16-byte chunks; slots outside [0, capacity) are skipped.
+__global__ __launch_bounds__(256) void prefill_append_kernel(const uint4* __restrict__ k_new,
+                                                             const uint4* __restrict__ v_new,
+                                                             uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                                                             const int32_t* __restrict__ start_arr, int n_kv_head,
+                                                             int q_len, int capacity, long total) {
+  constexpr int kChunks = D * 2 / 16;
+  const long idx = static_cast<long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= total) return;
+  const int c = static_cast<int>(idx % kChunks);
+  const long row = idx / kChunks;  // (b * n_kv_head + h) * q_len + t
+  const int t = static_cast<int>(row % q_len);
+  const long unit = row / q_len;
+  const int b = static_cast<int>(unit / n_kv_head);
+  const long p = static_cast<long>(start_arr != nullptr ? start_arr[b] : 0) + t;
+  if (p < 0 || p >= capacity) return;
+  const size_t dst = (static_cast<size_t>(unit) * capacity + static_cast<size_t>(p)) * kChunks + c;
+  k_cache[dst] = k_new[static_cast<size_t>(row) * kChunks + c];
+  v_cache[dst] = v_new[static_cast<size_t>(row) * kChunks + c];
+}
+
+template <class E, int G>
+hipError_t launch_prefill_g(const PrefillLaunch& p) {
+  const int rows = G * p.q_len;
+  const int row_tiles = (rows + kRowsWG - 1) / kRowsWG;
+  const int units = p.batch * p.n_kv_head;
+  hipLaunchKernelGGL((prefill_kernel<E, G>), dim3(row_tiles * units), dim3(256), 0, p.stream,
+                     static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k_cache),
+                     static_cast<const uint16_t*>(p.v_cache), p.start, static_cast<uint16_t*>(p.out), p.n_kv_head,
+                     p.q_len, p.capacity, units, row_tiles, p.scale_log2);
+  return hipGetLastError();
+}
+
+template <class E>
+hipError_t launch_prefill_e(const PrefillLaunch& p) {
+  switch (p.n_head / p.n_kv_head) {
+    case 1: return launch_prefill_g<E, 1>(p);
+    case 2: return launch_prefill_g<E, 2>(p);
+    case 3: return launch_prefill_g<E, 3>(p);
+    case 4: return launch_prefill_g<E, 4>(p);
+    case 5: return launch_prefill_g<E, 5>(p);
+    case 6: return launch_prefill_g<E, 6>(p);
+    case 7: return launch_prefill_g<E, 7>(p);
+    case 8: return launch_prefill_g<E, 8>(p);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillLaunch& p) {
+  return p.dtype == 1 ? launch_prefill_e<PBF16>(p) : launch_prefill_e<PF16>(p);
+}
+
+hipError_t launch_prefill_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                 const int32_t* start, int batch, int n_kv_head, int q_len, int capacity,
+                                 hipStream_t stream) {
+  const long total = static_cast<long>(batch) * n_kv_head * q_len * (D * 2 / 16);
+  const long blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(prefill_append_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new), static_cast<uint4*>(k_cache),
+                     static_cast<uint4*>(v_cache), start, n_kv_head, q_len, capacity, total);
+  return hipGetLastError();
+}
+
+}  // namespace ada

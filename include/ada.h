@@ -264,6 +264,52 @@ int ada_decode_step_rope(const void* q, const void* k_new, const void* v_new, co
                          void* workspace, size_t workspace_bytes, void* stream, int num_splits);
 
 /*
+ * Prompt append: the T prompt rows of every (batch row, KV head) written into
+ * slots start[b] .. start[b] + T - 1 of the preallocated caches, bit for bit
+ * ([ACTIVE-PREFIX] section 2: after the prompt prefill the cache holds
+ * kv_len = T slots; the allocation never changes). Slots outside
+ * [0, capacity) are skipped.
+ *
+ *   k_new, v_new  device, [batch, n_kv_head, q_len, head_dim].
+ *   k_cache,      device, [batch, n_kv_head, capacity, head_dim], updated in
+ *   v_cache       place.
+ *   start         device int32 [batch], or NULL: every row starts at slot 0.
+ * All buffers 16-byte aligned (ADA_ERR_ALIGN); head_dim 128. ADA_OK without
+ * work for batch == 0 or q_len == 0. One kernel launch on `stream`.
+ */
+int ada_prefill_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache, const int32_t* start,
+                       int batch, int n_kv_head, int q_len, int capacity, int head_dim, int dtype, void* stream);
+
+/*
+ * Causal prefill attention over the cache: q_len query tokens per batch row,
+ * token t at position start[b] + t attending cache slots 0 .. start[b] + t
+ * ([FORWARD-STEP] section 5: the batch prefill path runs attention with
+ * is_causal=True; with start = 0 this is that square causal mask over the
+ * prompt, and start > 0 continues a prompt after earlier tokens). The prompt's
+ * own rows must already be in the cache (ada_prefill_append). For token t of
+ * row b and query head h (KV head h / G, G = n_head / n_kv_head),
+ * n = clamp(start[b] + t + 1, 0, capacity):
+ *   out[b,h,t,:] = softmax_j(scale * q[b,h,t,:] . K[b,g,j,:]) V[b,g,j,:], j < n
+ * and n == 0 gives zeros. Scores and softmax statistics in fp32 (16-bit
+ * products are exact), softmax weights rounded once to the dtype for the
+ * weighted sum (the row sums use the same rounded weights), output rounded to
+ * nearest even.
+ *
+ *   q, out     device, [batch, n_head, q_len, head_dim] (the head-major query
+ *              of an SDPA call); out must not overlap the inputs.
+ *   k_cache,   device, [batch, n_kv_head, capacity, head_dim], read in place.
+ *   v_cache
+ *   start      device int32 [batch], or NULL: every row starts at slot 0.
+ *   scale      finite float (1/sqrt(head_dim) is SDPA's default).
+ * n_head a multiple of n_kv_head with n_head / n_kv_head in 1..8 (ADA_ERR_GQA);
+ * head_dim 128; buffers 16-byte aligned; ADA_OK without work for batch == 0
+ * or q_len == 0. One kernel launch on `stream`, no workspace.
+ */
+int ada_prefill_attn_gqa(const void* q, const void* k_cache, const void* v_cache, const int32_t* start, int batch,
+                         int n_head, int n_kv_head, int q_len, int head_dim, int capacity, float scale, int dtype,
+                         void* out, void* stream);
+
+/*
  * The two halves of a decode call, for callers that merge partial results
  * themselves -- e.g. key ranges held by different devices, whose partials are
  * concatenated along the split axis and combined once.

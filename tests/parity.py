@@ -35,6 +35,8 @@ def compare(got: torch.Tensor, want: np.ndarray) -> dict:
 def assert_parity(got: torch.Tensor, want: np.ndarray, dtype: str, what: str = "") -> dict:
     st = compare(got, want)
     max_abs, rel = TOL[dtype]
+    print(f"  parity {what}: max-abs {st['max_abs']:.2e} (tol {max_abs:.1e}), rel-Frobenius {st['rel_fro']:.2e} "
+          f"(tol {rel:.1e})", flush=True)
     assert st["finite"], f"{what}: non-finite GPU output"
     assert st["max_abs"] <= max_abs, f"{what}: max-abs {st['max_abs']:.3e} > {max_abs:.1e}"
     assert st["rel_fro"] <= rel, f"{what}: rel-Frobenius {st['rel_fro']:.3e} > {rel:.1e}"

@@ -207,6 +207,33 @@ def test_decode_step_rope_validation(ada):
     assert f(*args(splits=300)) == -8
 
 
+def test_prefill_validation(ada):
+    f = ada._lib.ada_prefill_attn_gqa
+    # q, k, v, start, B, Hq, Hkv, T, D, S, scale, dtype, out, stream
+    args = lambda **kw: [kw.get("q", P), kw.get("k", P2), kw.get("v", P3), NUL, kw.get("B", 1), kw.get("Hq", 32),
+                         kw.get("Hkv", 8), kw.get("T", 16), kw.get("D", 128), 64, ctypes.c_float(kw.get("scale", 0.08)),
+                         kw.get("dtype", 0), kw.get("out", P4), NUL]
+    assert f(*args(dtype=2)) == -4
+    assert f(*args(Hq=12)) == -3
+    assert f(*args(Hq=72)) == -3              # group 9
+    assert f(*args(D=64)) == -5
+    assert f(*args(T=-1)) == -2
+    assert f(*args(scale=float("inf"))) == -6
+    assert f(*args(q=NUL)) == -1
+    assert f(*args(out=NUL)) == -1
+    assert f(*args(q=MIS)) == -9
+    assert f(*args(T=0, q=NUL, k=NUL, v=NUL, out=NUL)) == 0
+    g = ada._lib.ada_prefill_append
+    gargs = lambda **kw: [kw.get("kn", P), P2, P3, P4, NUL, kw.get("B", 1), 8, kw.get("T", 16), 64, kw.get("D", 128),
+                          kw.get("dtype", 1), NUL]
+    assert g(*gargs(dtype=5)) == -4
+    assert g(*gargs(D=96)) == -5
+    assert g(*gargs(T=-3)) == -2
+    assert g(*gargs(kn=NUL)) == -1
+    assert g(*gargs(kn=MIS)) == -9
+    assert g(*gargs(T=0, kn=NUL)) == 0
+
+
 def test_workspace_bytes_arithmetic(ada):
     r256 = lambda x: (x + 255) // 256 * 256
     for B, Hq, Hkv, splits in ((1, 32, 8, 4), (8, 32, 8, 8), (4, 32, 8, 33), (1, 16, 16, 32), (3, 6, 3, 7)):
