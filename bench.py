@@ -18,7 +18,8 @@ not count, against 8 TB/s), the fp64 CPU oracle timed on a bounded sample of
 the same step, and, under "also", the per-kv_len figures, the
 long-context workload (batch 8, 32/8 heads, bf16, kv_len 32768, 1.07 GB per
 call), the 36-layer S2-Pro-shaped run, the full-capacity against
-active-prefix comparison, and the decode step with rotary embedding.
+active-prefix comparison, the decode step with rotary embedding, and the
+causal prompt prefill.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -404,6 +405,45 @@ def time_rope_step(ada, device, iters: int = 100) -> dict:
     return res
 
 
+PEAK_MFMA_16BIT_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
+
+
+def time_prefill(ada, device, iters: int = 30) -> dict:
+    """Prompt prefill (fish-speech #1310, section 2: kv_len = T after the
+    prompt; VoxCPM #395, section 5: causal attention): ada_prefill_attn_gqa
+    from slot 0 over a prompt already in the cache, averaged over back-to-back
+    launches bracketed by HIP events. Flops = 4 * D * H_q * B * T (T + 1) / 2
+    (q.k and p.v over the visible slots only), against the dense 16-bit MFMA
+    peak. Cases: the S2-Pro prompt (234 tokens, 32/8 heads, fp16, capacity
+    32768) and a 4096-token prompt (32/8 heads, bf16, capacity 8192)."""
+    res = {}
+    for name, B, Hq, Hkv, T, S, dtype in (("s2pro_prompt", 1, 32, 8, 234, 32768, "fp16"),
+                                          ("prompt_4096", 1, 32, 8, 4096, 8192, "bf16")):
+        D = 128
+        q = W.randn16((B, Hq, T, D), dtype, W.seed_for(2, 60_000), device=device)
+        k = W.randn16((B, Hkv, S, D), dtype, W.seed_for(2, 60_001), device=device)
+        v = W.randn16((B, Hkv, S, D), dtype, W.seed_for(2, 60_002), device=device)
+        out = torch.empty_like(q)
+        ada.prefill_attn_gqa(q, k, v, None, out=out)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(SPIN_CYCLES)
+        a.record()
+        for _ in range(iters):
+            ada.prefill_attn_gqa(q, k, v, None, out=out)
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / iters
+        flops = 4 * D * Hq * B * T * (T + 1) / 2
+        tfs = flops / us / 1e6
+        res[name] = {"workload": f"batch {B}, {Hq}/{Hkv} heads, head_dim {D}, {dtype}, prompt {T} tokens from slot 0, "
+                                 f"capacity {S}",
+                     "us": round(us, 2), "flops": int(flops), "TFLOPs": round(tfs, 1),
+                     "frac_of_mfma_peak": round(tfs / PEAK_MFMA_16BIT_TFLOPS, 4)}
+        del q, k, v, out
+    return res
+
+
 def cpu_baseline(seconds: float) -> dict:
     """The fp64 oracle on the same step (three decode calls of the sweep), run
     until ``seconds`` of CPU time have passed (at least one step)."""
@@ -505,6 +545,7 @@ def main(argv=None):
         also["s2pro_run"] = time_s2pro_run(ada, device)
         also["full_capacity_vs_active_prefix"] = time_full_vs_active(ada, device)
         also["rope_step"] = time_rope_step(ada, device)
+        also["prefill"] = time_prefill(ada, device)
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

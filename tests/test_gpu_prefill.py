@@ -163,3 +163,16 @@ def test_prefill_then_decode_pipeline(ada, ora):
         torch.cuda.synchronize()
         kc2, vc2 = ora.kv_append(kns, vns, to16(kc2), to16(vc2), [T + i])
         assert_parity(o, ora.decode(qs, to16(kc2), to16(vc2), [T + i + 1], 1 / math.sqrt(128)), "fp16", f"step {i}")
+
+
+def test_prefill_scale_edges(ada, ora):
+    """Scale 0 (every visible slot weighs the same: the running mean of the
+    value rows) and a negative scale, against the oracle."""
+    B, Hq, Hkv, T, S = 2, 8, 2, 70, 200
+    for scale, dtype in ((0.0, "fp16"), (-0.09, "bf16")):
+        say(f"case prefill scale={scale} {dtype}")
+        q, k, v = prefill_inputs(B, Hq, Hkv, T, S, dtype, [0, 60], 870)
+        out = ada.prefill_attn_gqa(q.cuda(), k.cuda(), v.cuda(), torch.tensor([0, 60], dtype=torch.int32,
+                                                                               device="cuda"), scale=scale)
+        torch.cuda.synchronize()
+        assert_parity(out, ora.prefill(q, k, v, [0, 60], scale), dtype, f"scale {scale}")
