@@ -230,6 +230,17 @@ int prepare_decode(const void* q, const void* k_cache, const void* v_cache, cons
   return ADA_OK;
 }
 
+// Rows per call up to which a call with device-side lengths uses the
+// balanced plan (each workgroup reads every row's length to find its range).
+constexpr int kBalancedMaxBatch = 64;
+
+// Use the balanced split plan? Only for heuristic split counts (a forced
+// count keeps the per-row ranges it asks for), lengths that only the device
+// knows, more than one row and at least two splits per row.
+bool use_balanced(const ada::DecodeLaunch& p, bool device_lengths, int num_splits) {
+  return device_lengths && num_splits == 0 && p.batch >= 2 && p.batch <= kBalancedMaxBatch && p.splits >= 2;
+}
+
 int check_workspace(const void* workspace, size_t workspace_bytes, int batch, int n_head,
                     int n_kv_head, int splits) {
   const ada::WorkspaceLayout w = ada::workspace_layout(batch, n_head, n_kv_head, ada::kHeadDim, splits);
@@ -262,10 +273,15 @@ int ada_decode_attn_gqa_ex(const void* q, const void* k_cache, const void* v_cac
     if (rc != ADA_OK) return rc;
     p.workspace = workspace;
   }
+  const bool balanced = use_balanced(p, kv_len != nullptr, num_splits);
+  if (balanced) p.chunk = 0;
   hipError_t e = ada::launch_partial(p);
   if (e != hipSuccess) return hip_fail(e);
   if (p.direct) return ADA_OK;
   ada::CombineLaunch c{workspace, out, batch, n_head, n_kv_head, p.splits, dtype, p.stream};
+  c.balanced = balanced;
+  c.kv_len = kv_len;
+  c.max_kv_len = p.max_kv_len;
   e = ada::launch_combine(c);
   return e == hipSuccess ? ADA_OK : hip_fail(e);
 }
@@ -311,10 +327,16 @@ int decode_step_impl(const void* q, const void* k_new, const void* v_new, const 
     if (rc != ADA_OK) return rc;
     p.workspace = workspace;
   }
+  const bool balanced = use_balanced(p, pos != nullptr, num_splits);
+  if (balanced) p.chunk = 0;
   hipError_t e = ada::launch_partial(p);
   if (e != hipSuccess) return hip_fail(e);
   if (p.direct) return ADA_OK;
   ada::CombineLaunch c{workspace, out, batch, n_head, n_kv_head, p.splits, dtype, p.stream};
+  c.balanced = balanced;
+  c.pos = pos;
+  c.step = true;
+  c.max_kv_len = p.max_kv_len;
   e = ada::launch_combine(c);
   return e == hipSuccess ? ADA_OK : hip_fail(e);
 }

@@ -43,7 +43,7 @@ struct DecodeLaunch {
   void* out;        // written when direct
   void* workspace;  // partials written when !direct
   int batch, n_head, n_kv_head, capacity, max_kv_len;
-  int splits, chunk;
+  int splits, chunk;  // chunk 0: balanced plan derived on the device from the row lengths
   bool direct;       // one split: write the output, no partials
   float scale_log2;  // scale * log2(e)
   int dtype;         // 0 fp16, 1 bf16
@@ -56,6 +56,13 @@ struct CombineLaunch {
   int batch, n_head, n_kv_head, splits;
   int dtype;
   hipStream_t stream;
+  // Balanced plan (the partial launch had chunk == 0): the row lengths it
+  // was derived from, so the combine derives the same plan.
+  bool balanced = false;
+  const int32_t* kv_len = nullptr;
+  const int32_t* pos = nullptr;
+  bool step = false;  // lengths are pos + 1 (decode step)
+  int max_kv_len = 0;
 };
 
 struct PrefillLaunch {

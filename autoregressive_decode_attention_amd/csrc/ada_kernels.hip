@@ -264,11 +264,52 @@ __device__ __forceinline__ uint4 rope_chunk(const uint16_t* row, const uint16_t*
 // live prefix is p + 1 slots. Otherwise lengths come from kv_len, or are
 // max_kv_len for every row when kv_len is NULL (one position for the whole
 // batch: nothing is read before the K/V stream starts).
+// Live slots of batch row b: pos[b] + 1 for a decode step (pos NULL: all
+// rows at slot max_kv_len - 1), else kv_len[b] (NULL: max_kv_len), clamped
+// to [0, max_kv_len].
+__device__ __forceinline__ int row_length(const int32_t* kv_len, const int32_t* pos, bool step, int max_kv_len,
+                                          int b) {
+  int n = max_kv_len;
+  if (step) {
+    n = (pos != nullptr ? pos[b] : max_kv_len - 1) + 1;
+  } else if (kv_len != nullptr) {
+    n = kv_len[b];
+  }
+  return n < 0 ? 0 : (n > max_kv_len ? max_kv_len : n);
+}
+
+// Balanced split plan for batches whose lengths live on the device (so the
+// host cannot size the splits per row): the `slots` workgroups of a KV head
+// are shared by all rows with one common chunk c (a multiple of the 64-slot
+// tile), row b taking ceil(n_b / c) consecutive slots. c is the smallest
+// multiple of 64 from ceil(total / slots) on for which the rows fit (tried 8
+// times), else ceil(total / (slots - batch)) rounded up, which always fits
+// (each row wastes less than one chunk). Every kernel of a call derives the
+// same plan from the same lengths.
+__device__ __forceinline__ int balanced_chunk(const int32_t* kv_len, const int32_t* pos, bool step, int max_kv_len,
+                                              int batch, int slots) {
+  long total = 0;
+  for (int b = 0; b < batch; ++b) total += row_length(kv_len, pos, step, max_kv_len, b);
+  long c = (total + slots - 1) / slots;
+  c = c < kTileRows ? kTileRows : (c + kTileRows - 1) / kTileRows * kTileRows;
+  for (int tries = 0; tries < 8; ++tries, c += kTileRows) {
+    long used = 0;
+    for (int b = 0; b < batch; ++b) used += (row_length(kv_len, pos, step, max_kv_len, b) + c - 1) / c;
+    if (used <= slots) return static_cast<int>(c);
+  }
+  const long free = slots - batch;  // >= batch: the host asks for >= 2 slots per row
+  long safe = (total + free - 1) / free;
+  safe = safe < kTileRows ? kTileRows : (safe + kTileRows - 1) / kTileRows * kTileRows;
+  return static_cast<int>(safe);
+}
+
 struct SplitRange {
   int n;          // live slots of this batch row
   int row_begin;  // this split's first slot
   int last_row;   // this split's last live slot
   int p_new;      // slot appended by this call, or -1
+  int split;      // this workgroup's split of its row (0 writes the appended row)
+  int b;          // batch row (not the grid's z index under the balanced plan)
   size_t head_off;   // (b, g) head of the caches, in elements
   size_t new_row;    // (b, g) row of k_new / v_new, in elements
   size_t out_row0;   // first output element of the group's query heads
@@ -285,11 +326,30 @@ __device__ __forceinline__ bool begin_split(SplitRange& r, uint16_t* k_cache, ui
                                             float2* part_ml, int n_kv_head, int capacity, int max_kv_len,
                                             int chunk, int direct) {
   constexpr int D = kHeadDim;
-  const int split = blockIdx.x;
   const int g = blockIdx.y;
-  const int b = blockIdx.z;
   const int tid = threadIdx.x;
   const int n_head = n_kv_head * G;
+  int split = blockIdx.x;
+  int b = blockIdx.z;
+  size_t slot = static_cast<size_t>(split) * gridDim.z + b;  // partial slot (split-major)
+  if (chunk == 0) {
+    // Balanced plan: this workgroup is slot z * splits + x of its KV head.
+    const int idx = blockIdx.z * gridDim.x + blockIdx.x;
+    chunk = balanced_chunk(kv_len, pos, k_new != nullptr, max_kv_len, gridDim.z, gridDim.x * gridDim.z);
+    int first = 0;
+    b = -1;
+    for (int bb = 0; bb < static_cast<int>(gridDim.z); ++bb) {
+      const int sb = (row_length(kv_len, pos, k_new != nullptr, max_kv_len, bb) + chunk - 1) / chunk;
+      if (idx < first + sb) {
+        b = bb;
+        split = idx - first;
+        break;
+      }
+      first += sb;
+    }
+    if (b < 0) return false;  // a slot no row needs: nothing to write
+    slot = idx;
+  }
   r.head_off = (static_cast<size_t>(b) * n_kv_head + g) * static_cast<size_t>(capacity) * D;
   r.new_row = (static_cast<size_t>(b) * n_kv_head + g) * D;
   r.p_new = -1;
@@ -316,7 +376,7 @@ __device__ __forceinline__ bool begin_split(SplitRange& r, uint16_t* k_cache, ui
   const int nsplit = (r.n + chunk - 1) / chunk;  // splits holding live slots
   const size_t head_row0 = static_cast<size_t>(b) * n_head + static_cast<size_t>(g) * G;
   r.out_row0 = head_row0 * D;
-  r.part_row0 = static_cast<size_t>(split) * gridDim.z * n_head + head_row0;  // split-major partials
+  r.part_row0 = slot * n_head + static_cast<size_t>(g) * G;  // slot-major partials
   if (split >= nsplit) {
     if (direct) {
       for (int idx = tid; idx < G * D; idx += kThreads) out[r.out_row0 + idx] = 0;
@@ -325,6 +385,8 @@ __device__ __forceinline__ bool begin_split(SplitRange& r, uint16_t* k_cache, ui
     }
     return false;
   }
+  r.split = split;
+  r.b = b;
   r.row_begin = split * chunk;
   r.last_row = min(r.row_begin + chunk, r.n) - 1;
   return true;
@@ -607,10 +669,9 @@ __global__ __launch_bounds__(kThreads) void partial_kernel(
       const int h = tid / 16;
       const int c = tid % 16;
       const uint16_t* row = h < G ? q + r.out_row0 + static_cast<size_t>(h) * D : k_new + r.new_row;
-      const uint4 v = rope_chunk<E>(row, cs + static_cast<size_t>(blockIdx.z) * D,
-                                    sn + static_cast<size_t>(blockIdx.z) * D, 8 * c);
+      const uint4 v = rope_chunk<E>(row, cs + static_cast<size_t>(r.b) * D, sn + static_cast<size_t>(r.b) * D, 8 * c);
       s_rot[h][c] = v;
-      if (h == G && blockIdx.x == 0 && p_new >= 0 && p_new < capacity)
+      if (h == G && r.split == 0 && p_new >= 0 && p_new < capacity)
         *reinterpret_cast<uint4*>(k_cache + r.head_off + static_cast<size_t>(p_new) * D + 8 * c) = v;
     }
     __syncthreads();
@@ -675,7 +736,9 @@ __device__ __forceinline__ float2 buffer_load_f2(__amdgpu_buffer_rsrc_t r, uint3
 template <class E>
 __global__ __launch_bounds__(64 * kMaxGroup) void combine_kernel(
     uint16_t* __restrict__ out, const float2* __restrict__ part_ml,
-    const float* __restrict__ part_acc, int n_kv_head, int group, int num_splits) {
+    const float* __restrict__ part_acc, int n_kv_head, int group, int num_splits,
+    const int32_t* __restrict__ kv_len, const int32_t* __restrict__ pos, int step, int max_kv_len,
+    int balanced) {
   constexpr int D = kHeadDim;
   constexpr int kBatch = 32;  // the heuristic rarely asks for more: one memory wait
   const int g = blockIdx.x;
@@ -684,7 +747,20 @@ __global__ __launch_bounds__(64 * kMaxGroup) void combine_kernel(
   const int i = threadIdx.x >> 6;  // query head within the group
   const int n_head = n_kv_head * group;
   const uint32_t head_row = static_cast<uint32_t>(b) * n_head + static_cast<uint32_t>(g) * group + i;
-  const uint32_t split_stride = static_cast<uint32_t>(gridDim.y) * n_head;  // split-major partials
+  // Partial entry of split s: slot * n_head + g * group + i, where the slot
+  // is s * batch + b (split-major), or first_slot(b) + s under the balanced
+  // plan (the row's consecutive slots).
+  uint32_t row0 = head_row;
+  uint32_t split_stride = static_cast<uint32_t>(gridDim.y) * n_head;
+  if (balanced) {
+    const int slots = num_splits * static_cast<int>(gridDim.y);
+    const int chunk = balanced_chunk(kv_len, pos, step != 0, max_kv_len, gridDim.y, slots);
+    int first = 0;
+    for (int bb = 0; bb < b; ++bb) first += (row_length(kv_len, pos, step != 0, max_kv_len, bb) + chunk - 1) / chunk;
+    num_splits = (row_length(kv_len, pos, step != 0, max_kv_len, b) + chunk - 1) / chunk;
+    row0 = static_cast<uint32_t>(first) * n_head + static_cast<uint32_t>(g) * group + i;
+    split_stride = n_head;
+  }
   const __amdgpu_buffer_rsrc_t ml_r = workspace_rsrc(part_ml);
   const __amdgpu_buffer_rsrc_t acc_r = workspace_rsrc(part_acc);
 
@@ -696,7 +772,7 @@ __global__ __launch_bounds__(64 * kMaxGroup) void combine_kernel(
     for (int k = 0; k < kBatch; ++k) {
       const int s = s0 + k;
       if (s < num_splits) {
-        const uint32_t row = head_row + static_cast<uint32_t>(s) * split_stride;
+        const uint32_t row = row0 + static_cast<uint32_t>(s) * split_stride;
         ml[k] = buffer_load_f2(ml_r, row * 8u);
         a[k] = buffer_load_f2(acc_r, row * (D * 4u) + lane * 8u);
       } else {
@@ -840,9 +916,11 @@ hipError_t launch_combine_impl(const CombineLaunch& p) {
   uint16_t* out = static_cast<uint16_t*>(p.out);
   const dim3 grid(p.n_kv_head, p.batch), block(64 * group);
   if (p.dtype == 1) {
-    hipLaunchKernelGGL(combine_kernel<BF16>, grid, block, 0, p.stream, out, ml, acc, p.n_kv_head, group, p.splits);
+    hipLaunchKernelGGL(combine_kernel<BF16>, grid, block, 0, p.stream, out, ml, acc, p.n_kv_head, group, p.splits,
+                       p.kv_len, p.pos, p.step ? 1 : 0, p.max_kv_len, p.balanced ? 1 : 0);
   } else {
-    hipLaunchKernelGGL(combine_kernel<F16>, grid, block, 0, p.stream, out, ml, acc, p.n_kv_head, group, p.splits);
+    hipLaunchKernelGGL(combine_kernel<F16>, grid, block, 0, p.stream, out, ml, acc, p.n_kv_head, group, p.splits,
+                       p.kv_len, p.pos, p.step ? 1 : 0, p.max_kv_len, p.balanced ? 1 : 0);
   }
   return hipGetLastError();
 }

@@ -17,7 +17,8 @@ bracketed by HIP events, with the host queued ahead so that launch cost does
 not count, against 8 TB/s), the fp64 CPU oracle timed on a bounded sample of
 the same step, and, under "also", the per-kv_len figures, the
 long-context workload (batch 8, 32/8 heads, bf16, kv_len 32768, 1.07 GB per
-call), the 36-layer S2-Pro-shaped run, the full-capacity against
+call), the 36-layer S2-Pro-shaped run, the MiniCPM-shaped streaming
+workload (lockstep positions and ragged batches), the full-capacity against
 active-prefix comparison, the decode step with rotary embedding, and the
 causal prompt prefill.
 
@@ -405,6 +406,61 @@ def time_rope_step(ada, device, iters: int = 100) -> dict:
     return res
 
 
+def time_minicpm_stream(ada, device, iters: int = 50, draws: int = 16) -> dict:
+    """The MiniCPM-shaped streaming workload (batch 4, 32/8 heads, bf16,
+    capacity 8192; VoxCPM #395, sections 2.2 and 6.3): (a) lockstep decode
+    steps (append at position p, attend over p + 1 slots, one host position
+    for the batch) at p = 4095 and 8191; (b) ragged batches, per-row kv_len
+    drawn uniformly from [1, 8192] (seeded), lengths on the device. Each
+    figure is the average over back-to-back calls bracketed by HIP events,
+    with caches rotated so every call reads HBM; GB/s counts the live slots
+    only."""
+    shp = W.WORKLOADS["minicpm_stream"].shape
+    B, Hq, Hkv, D, S = shp.batch, shp.n_head, shp.n_kv_head, shp.head_dim, shp.capacity
+    R = max(2, math.ceil(2 * MALL_BYTES / kv_bytes(Hkv, D, B * S)))
+    xs = [W.decode_inputs(shp, [S] * B, W.seed_for(3, 70_000 + r), device=device, tail="random") for r in range(R)]
+    k_new, v_new = W.append_inputs(B, Hkv, D, shp.dtype, W.seed_for(3, 71_000), device=device)
+    ws = ada.new_workspace(ada.decode_workspace_bytes(B, Hq, Hkv, D, 256), device)
+    out = torch.empty_like(xs[0]["q"])
+    scale = 1.0 / math.sqrt(D)
+
+    def timed(fn):
+        fn(0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(SPIN_CYCLES)
+        a.record()
+        for i in range(iters):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / iters
+
+    res = {"workload": "minicpm_stream: batch 4, 32/8 heads, head_dim 128, bf16, capacity 8192"}
+    for p in (4095, 8191):
+        us = timed(lambda i, p=p: ada.decode_step(xs[i % R]["q"], k_new, v_new, xs[i % R]["k_cache"],
+                                                  xs[i % R]["v_cache"], p, scale=scale, out=out, workspace=ws))
+        nb = decode_bytes(B, Hq, Hkv, D, [p + 1] * B)
+        res[f"lockstep_p{p}"] = {"us": round(us, 2), "GBs": round(nb / us / 1e3, 1),
+                                 "frac_of_peak": round(nb / us / 1e3 / PEAK_HBM_GBS, 4)}
+    rows = []
+    for d in range(draws):
+        lens = W.ragged_lengths(B, 1, S, W.seed_for(3, 72_000 + d))
+        lt = torch.tensor(lens, dtype=torch.int32, device=device)
+        us = timed(lambda i, lt=lt: ada.decode_attn_gqa(xs[i % R]["q"], xs[i % R]["k_cache"], xs[i % R]["v_cache"],
+                                                         lt, scale=scale, out=out, max_kv_len=S, workspace=ws))
+        rows.append((lens, us, decode_bytes(B, Hq, Hkv, D, lens)))
+    tot_b = sum(r[2] for r in rows)
+    tot_us = sum(r[1] for r in rows)
+    big = [r for r in rows if sum(r[0]) / B >= 4096]
+    res["ragged"] = {"draws": draws, "mean_us": round(tot_us / draws, 2), "GBs": round(tot_b / tot_us / 1e3, 1),
+                     "frac_of_peak": round(tot_b / tot_us / 1e3 / PEAK_HBM_GBS, 4),
+                     "draws_mean_len_ge_4096": len(big),
+                     "GBs_mean_len_ge_4096": round(sum(r[2] for r in big) / max(1e-9, sum(r[1] for r in big)) / 1e3, 1)}
+    del xs
+    return res
+
+
 PEAK_MFMA_16BIT_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 matrix peak
 
 
@@ -544,6 +600,7 @@ def main(argv=None):
         also["long_context"] = time_long_context(ada, device)
         also["s2pro_run"] = time_s2pro_run(ada, device)
         also["full_capacity_vs_active_prefix"] = time_full_vs_active(ada, device)
+        also["minicpm_stream"] = time_minicpm_stream(ada, device)
         also["rope_step"] = time_rope_step(ada, device)
         also["prefill"] = time_prefill(ada, device)
 

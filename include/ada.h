@@ -198,7 +198,17 @@ size_t ada_decode_workspace_bytes(int batch, int n_head, int n_kv_head, int head
  * kernel writes per-split results to the workspace and a combine kernel
  * merges them (log-sum-exp weights, split order). Scores, softmax
  * statistics and accumulators are fp32. The result is bitwise deterministic
- * for a given split count.
+ * for a given split count and given lengths.
+ *
+ * Balanced plan: with device lengths (kv_len != NULL), 2..64 batch rows and
+ * two or more heuristic splits, the splits * batch workgroups of each KV head
+ * are shared among the rows in proportion to their lengths rather than
+ * `splits` per row: both kernels derive one common range length from
+ * kv_len on the device (no host synchronisation) and row b takes
+ * ceil(n_b / range) consecutive workgroups. Ragged batches then spread their
+ * keys over all workgroups; the workspace size is unchanged. A forced split
+ * count (ada_decode_attn_gqa_ex with num_splits > 0) and ada_decode_partial
+ * keep the per-row plan.
  */
 int ada_decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* kv_len, int batch, int n_head, int n_kv_head,

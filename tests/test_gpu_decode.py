@@ -371,13 +371,18 @@ def test_partial_then_combine_equals_decode(ada, ora):
                                       max_kv_len=3000, num_splits=splits)
         out = torch.empty_like(x["q"])
         ada.decode_combine(ws, used, out, n_kv_head=8)
-        # same plan as the partial call: the heuristic when splits == 0, else forced
         ref = ada.decode_attn_gqa_ex(x["q"], x["k_cache"], x["v_cache"], x["kv_len"], scale=SCALE,
                                      max_kv_len=3000, num_splits=splits)
-        if used > 1:
+        if used > 1 and splits > 0:  # same forced plan: bit for bit
             assert torch.equal(out, ref), f"partial+combine differs from the decode call at {used} splits"
-        else:  # one split: the decode call writes directly, the combine divides once more
-            assert_parity(out, to_f64(ref), "bf16", "one split via combine")
+        else:
+            # one split: the decode call writes directly, the combine divides once more;
+            # heuristic count with device lengths: the decode call shares the workgroups
+            # among the rows by length (balanced plan), the explicit partial keeps one
+            # range plan per row -- the same keys, split differently
+            assert_parity(out, to_f64(ref), "bf16", f"partial+combine vs decode call, splits={splits}")
+            assert_parity(out, ora.decode(x["q"].cpu(), x["k_cache"].cpu(), x["v_cache"].cpu(), lens, SCALE),
+                          "bf16", "partial+combine vs oracle")
 
 
 def test_key_ranges_merged_by_combine(ada, ora):
@@ -536,3 +541,36 @@ def test_graph_replayed_steps_match_eager(ada, ora):
                 to16 = lambda a: torch.from_numpy(a.view(np.int16)).view(dt)
                 want = ora.decode(xs[l]["q"], to16(kc), to16(vc), [T0 + 1] * B, SCALE)
                 assert_parity(out_g[l], want, "fp16", f"graph layer {l}")
+
+
+def test_balanced_plan_for_device_lengths(ada, ora):
+    """Device-side lengths with 2..64 rows use the balanced split plan (each KV
+    head's workgroups shared among the rows by length): ragged, empty and
+    clamped rows, a single long row among empty ones, 64 rows, and 65 rows
+    (the per-row plan again); decode steps with per-row positions too."""
+    cases = [
+        (shape(4, 32, 8, 8192, "bf16"), [8192, 17, 0, 5000], "ragged with an empty row"),
+        (shape(8, 32, 8, 4096, "fp16"), [0, 0, 0, 4096, 0, 0, 0, 0], "one long row"),
+        (shape(8, 16, 16, 2048, "fp16"), [0] * 8, "all empty"),
+        (shape(64, 8, 2, 512, "bf16"), [int(x) for x in np.random.default_rng(5).integers(0, 513, 64)], "64 rows"),
+        (shape(65, 8, 2, 256, "fp16"), [int(x) for x in np.random.default_rng(6).integers(1, 257, 65)], "65 rows"),
+        (shape(3, 32, 8, 300, "bf16"), [300, 299, 1], "short rows"),
+    ]
+    for k, (shp, lens, what) in enumerate(cases):
+        run(ada, ora, shp, lens, 980 + k, splits=0, what=f"balanced {what}")
+    # decode steps with per-row positions (balanced), out-of-range positions included
+    B, Hq, Hkv, D, S = 6, 32, 8, 128, 4096
+    pos = [4095, 10, -1, 2000, 4096, 0]
+    say(f"case balanced decode step pos={pos}")
+    lens = [S if p >= S else max(0, p) for p in pos]
+    x = W.decode_inputs(W.DecodeShape(B, Hq, Hkv, D, S, "bf16"), lens, 990, tail="nan")
+    kn, vn = W.append_inputs(B, Hkv, D, "bf16", 991)
+    d = gpu(x)
+    out = ada.decode_step(d["q"], kn.cuda(), vn.cuda(), d["k_cache"], d["v_cache"],
+                          torch.tensor(pos, dtype=torch.int32, device="cuda"), scale=SCALE)
+    torch.cuda.synchronize()
+    kc, vc = ora.kv_append(kn, vn, x["k_cache"], x["v_cache"], pos)
+    to16 = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    eff = [min(p, S - 1) + 1 if p >= 0 else 0 for p in pos]
+    assert_parity(out, ora.decode(x["q"], to16(kc), to16(vc), eff, SCALE), "bf16", "balanced decode step")
+    assert np.array_equal(d["k_cache"].cpu().view(torch.int16).numpy().view(np.uint16), kc)
