@@ -23,14 +23,9 @@
 //   * S^T = K Q^T with v_mfma_f32_16x16x32 (16-bit inputs, fp32 sums): keys
 //     on M, query rows on N, head dims on K. A lane then holds, for one query
 //     row, 16 scores (4 keys in each of the tile's four 16-key blocks).
-//   * Online softmax in base 2 per row in fp32 against a running reference
-//     that may trail the true maximum by up to 2^8 (the output rows are
-//     rescaled only when a score exceeds it by more); the weights are rounded
-//     once to the 16-bit type and the row sums use the rounded weights, so
-//     numerator and denominator see the same values.
-//   * K/V tiles are double-buffered in LDS: tile i is computed while tile
-//     i + 1 is stored from registers and tile i + 2 is loaded, one barrier
-//     per tile.
+//   * Online softmax in base 2 per row in fp32, exact running maximum; the
+//     weights are rounded once to the 16-bit type and the row sums use the
+//     rounded weights, so numerator and denominator see the same values.
 //   * O += P V with the same instruction: P is the A operand straight from
 //     registers, its K index running over the lane's 8 keys of a 32-key step
 //     (a fixed permutation of the keys, the same one the V operand uses).
@@ -38,6 +33,12 @@
 //     8 keys of one dim as two 8-byte loads.
 //   * Row statistics move from the score layout (row = lane % 16) to the
 //     output layout (rows 4 * (lane / 16) + j) with ds_bpermute.
+//   * A tile is a fraction of a microsecond of matrix work while its loads
+//     (mostly L2 hits) take longer, so the kernel leans on occupancy to
+//     overlap them: one 35 KB LDS tile per workgroup (loaded into registers
+//     one tile ahead, two barriers per tile) and registers capped for three
+//     wavefronts per SIMD. Measured on MI355X this beat double-buffered LDS
+//     at two per SIMD by 14 % (4096-8192-token prompts); four per SIMD spill.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -73,11 +74,11 @@ struct PBF16 {
 };
 
 constexpr int D = kHeadDim;     // 128
+constexpr int kRowsWG = 64;      // query rows per workgroup
 constexpr int kKeys = 64;        // key/value slots per tile
 constexpr int kKStride = D + 8;  // K tile row stride in LDS (u16): 272 B, 4-bank rotation per row
 constexpr int kVStride = 68;     // transposed V row stride (u16): 34 dwords, 2-bank rotation per row
 constexpr float kNegInf = -__builtin_inff();
-constexpr float kSlack = 8.0f;  // base-2 headroom before the output rows are rescaled
 
 __device__ __forceinline__ float finite_ref(float m) { return m == kNegInf ? 0.0f : m; }
 
@@ -110,17 +111,15 @@ __device__ __forceinline__ int visible(int start, int t, int capacity) {
   return n < 0 ? 0 : (n > capacity ? capacity : static_cast<int>(n));
 }
 
-template <class E, int G, int RB>
-__global__ __launch_bounds__(256) void prefill_kernel(const uint16_t* __restrict__ q,
+template <class E, int G>
+__global__ __launch_bounds__(256, 3) void prefill_kernel(const uint16_t* __restrict__ q,
                                                       const uint16_t* __restrict__ k_cache,
                                                       const uint16_t* __restrict__ v_cache,
                                                       const int32_t* __restrict__ start_arr,
                                                       uint16_t* __restrict__ out, int n_kv_head, int q_len,
                                                       int capacity, int units, int row_tiles, float scale_log2) {
-  constexpr int kRowsWave = 16 * RB;
-  constexpr int kRowsWG = 4 * kRowsWave;
-  __shared__ __align__(16) uint16_t s_k[2][kKeys * kKStride];  // double-buffered tiles
-  __shared__ __align__(16) uint16_t s_vt[2][D * kVStride];
+  __shared__ __align__(16) uint16_t s_k[kKeys * kKStride];
+  __shared__ __align__(16) uint16_t s_vt[D * kVStride];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -144,32 +143,25 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint16_t* __restrict
   const size_t head_off = static_cast<size_t>(unit) * capacity * D;
   const uint16_t* kbase = k_cache + head_off;
   const uint16_t* vbase = v_cache + head_off;
-  const int rw0 = r0 + wave * kRowsWave;  // the wave's first row
 
-  // Per row block rb: this lane's query row in the score layout is
-  // rw0 + 16*rb + lr; Q^T operand = dims 32*ks + 8*a .. + 8 of that row.
-  uint4 qb[RB][4];
-  int my_n[RB];
+  // This lane's query row in the score layout (row lr of the wave's 16).
+  const int my_row = r0 + wave * 16 + lr;
+  const int my_t = my_row / G;
+  const bool row_ok = my_row < rows;
+  const int my_n = row_ok ? visible(start, my_t, capacity) : 0;
+  uint4 qb[4];  // Q^T operand: dims 32*ks + 8*a .. + 8 of row my_row
+  {
+    const int i = my_row % G;
+    const uint16_t* qrow = q + ((static_cast<size_t>(b) * n_head + g * G + i) * q_len + (row_ok ? my_t : 0)) * D;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int row = rw0 + 16 * rb + lr;
-    const bool ok = row < rows;
-    const int t = row / G;
-    my_n[rb] = ok ? visible(start, t, capacity) : 0;
-    const uint16_t* qrow = q + ((static_cast<size_t>(b) * n_head + g * G + row % G) * q_len + (ok ? t : 0)) * D;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qb[rb][ks] = ok ? ld16(qrow + 32 * ks + 8 * a) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < 4; ++ks) qb[ks] = row_ok ? ld16(qrow + 32 * ks + 8 * a) : make_uint4(0, 0, 0, 0);
   }
 
-  f4 o[RB][8];
-  float m_run[RB], l_run[RB];  // running reference (same in a row's 4 lanes), this lane's share of the row sum
+  f4 o[8];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = kNegInf;
-    l_run[rb] = 0.0f;
-#pragma unroll
-    for (int db = 0; db < 8; ++db) o[rb][db] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-  }
+  for (int db = 0; db < 8; ++db) o[db] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+  float m_run = kNegInf;  // running max of row my_row (same in its 4 lanes)
+  float l_run = 0.0f;     // this lane's share of the row's weight sum
 
   // Tile staging: K as 4 row chunks per thread (16 threads per 256-byte row),
   // V as two rows x one 16-byte chunk (key pair kp, dims 8c .. 8c + 8) twice.
@@ -192,13 +184,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint16_t* __restrict
       vreg[it][1] = ld16(vbase + static_cast<size_t>(k1) * D + 8 * c);
     }
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* sk = s_k[buf];
-    uint16_t* svt = s_vt[buf];
+  auto store_tile = [&]() {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int idx = tid + 256 * it;
-      *reinterpret_cast<uint4*>(sk + (idx / 16) * kKStride + 8 * (idx % 16)) = kreg[it];
+      *reinterpret_cast<uint4*>(s_k + (idx / 16) * kKStride + 8 * (idx % 16)) = kreg[it];
     }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -211,134 +201,104 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint16_t* __restrict
         // dims 8c + 2w (low halves) and 8c + 2w + 1 (high halves) of keys 2kp, 2kp + 1
         const uint32_t lo = (r0w[w] & 0xffffu) | (r1w[w] << 16);
         const uint32_t hi = (r0w[w] >> 16) | (r1w[w] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(svt + (8 * c + 2 * w) * kVStride + 2 * kp) = lo;
-        *reinterpret_cast<uint32_t*>(svt + (8 * c + 2 * w + 1) * kVStride + 2 * kp) = hi;
+        *reinterpret_cast<uint32_t*>(s_vt + (8 * c + 2 * w) * kVStride + 2 * kp) = lo;
+        *reinterpret_cast<uint32_t*>(s_vt + (8 * c + 2 * w + 1) * kVStride + 2 * kp) = hi;
       }
     }
   };
 
-  // Pipeline: tile i is computed from LDS buffer i % 2 while tile i + 1
-  // waits in registers and tile i + 2's loads are in flight; one barrier per
-  // tile separates a buffer's reads (iteration i) from its next writes (i + 1).
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-    if (ntiles > 1) load_tile(1);
-    __syncthreads();
-  }
+  if (ntiles > 0) load_tile(0);
   for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    const uint16_t* sk = s_k[buf];
-    const uint16_t* svt = s_vt[buf];
+    __syncthreads();  // every wave is done with the previous tile
+    store_tile();
+    __syncthreads();
+    if (tile + 1 < ntiles) load_tile(tile + 1);
     const int base = tile * kKeys;
 
-    // S^T = K Q^T: block nb holds keys base + 16*nb + 4*a + j; each K operand
-    // read from LDS serves the RB row blocks.
-    f4 s[RB][4];
+    // S^T = K Q^T: block nb holds keys base + 16*nb + 4*a + j for row my_row.
+    f4 s[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      s[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 kop = *reinterpret_cast<const uint4*>(s_k + (16 * nb + lr) * kKStride + 32 * ks + 8 * a);
+        s[nb] = E::mma(kop, qb[ks], s[nb]);
+      }
+    }
+    // Scale, mask (slots past the row's own position), tile maximum.
+    float x[4][4];
+    float mx = kNegInf;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) s[rb][nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 kop = *reinterpret_cast<const uint4*>(sk + (16 * nb + lr) * kKStride + 32 * ks + 8 * a);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[rb][nb] = E::mma(kop, qb[rb][ks], s[rb][nb]);
+      for (int j = 0; j < 4; ++j) {
+        const int key = base + 16 * nb + 4 * a + j;
+        x[nb][j] = key < my_n ? s[nb][j] * scale_log2 : kNegInf;
+        mx = fmaxf(mx, x[nb][j]);
       }
     }
-    uint4 pa[RB][2];
+    mx = xor32_max(xor16_max(mx));  // over the row's 4 lanes
+    const float m_new = fmaxf(m_run, mx);
+    const float ref = finite_ref(m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - ref);  // 0 while nothing was seen
+    m_run = m_new;
+    l_run *= alpha;
+    // Weights, rounded to the 16-bit type, packed as the A operand of P V:
+    // step ks2 holds keys base + 32*ks2 + 4*a + j (first half) and
+    // base + 32*ks2 + 16 + 4*a + j (second half), j = 0..3.
+    uint4 pa[2];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      // Scale, mask (slots past the row's own position), tile maximum.
-      float x[4][4];
-      float mx = kNegInf;
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      uint32_t w[4];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
+      for (int h = 0; h < 2; ++h) {
+        const int nb = 2 * ks2 + h;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int key = base + 16 * nb + 4 * a + j;
-          x[nb][j] = key < my_n[rb] ? s[rb][nb][j] * scale_log2 : kNegInf;
-          mx = fmaxf(mx, x[nb][j]);
+        for (int jj = 0; jj < 2; ++jj) {
+          const uint32_t p0 = E::round(__builtin_amdgcn_exp2f(x[nb][2 * jj] - ref));
+          const uint32_t p1 = E::round(__builtin_amdgcn_exp2f(x[nb][2 * jj + 1] - ref));
+          l_run += E::to_float(p0) + E::to_float(p1);
+          w[2 * h + jj] = p0 | (p1 << 16);
         }
       }
-      mx = xor32_max(xor16_max(mx));  // over the row's 4 lanes
-      // The reference need not be the exact maximum: weights up to 2^kSlack
-      // are harmless, so the output rows are rescaled only when some row of
-      // the block sees a score more than kSlack above its reference (always
-      // on a row's first visible tile).
-      const bool grow = mx > m_run[rb] + kSlack;
-      if (__any(grow)) {
-        const float m_new = grow ? mx : m_run[rb];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - finite_ref(m_new));  // 0 while nothing was seen
-        m_run[rb] = m_new;
-        l_run[rb] *= alpha;
-        float al[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) al[j] = from_lane(alpha, 4 * a + j);
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[rb][db][j] *= al[j];
-        }
-      }
-      const float ref = finite_ref(m_run[rb]);
-      // Weights, rounded to the 16-bit type, packed as the A operand of P V:
-      // step ks2 holds keys base + 32*ks2 + 4*a + j (first half) and
-      // base + 32*ks2 + 16 + 4*a + j (second half), j = 0..3.
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        uint32_t w[4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int nb = 2 * ks2 + h;
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const uint32_t p0 = E::round(__builtin_amdgcn_exp2f(x[nb][2 * jj] - ref));
-            const uint32_t p1 = E::round(__builtin_amdgcn_exp2f(x[nb][2 * jj + 1] - ref));
-            l_run[rb] += E::to_float(p0) + E::to_float(p1);
-            w[2 * h + jj] = p0 | (p1 << 16);
-          }
-        }
-        pa[rb][ks2] = make_uint4(w[0], w[1], w[2], w[3]);
-      }
+      pa[ks2] = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    // O += P V: B operand = V at the same 8 keys, dim 16*db + lr; each V
-    // operand read from LDS serves the RB row blocks.
+    // Rescale the output rows this lane holds (rows 4*a + j of the wave).
+    float al[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) al[j] = from_lane(alpha, 4 * a + j);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) o[db][j] *= al[j];
+    }
+    // O += P V: B operand = V at the same 8 keys, dim 16*db + lr.
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const uint16_t* vrow = svt + (16 * db + lr) * kVStride + 32 * ks2 + 4 * a;
+        const uint16_t* vrow = s_vt + (16 * db + lr) * kVStride + 32 * ks2 + 4 * a;
         const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
         const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
-        const uint4 vop = make_uint4(v0.x, v0.y, v1.x, v1.y);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[rb][db] = E::mma(pa[rb][ks2], vop, o[rb][db]);
+        o[db] = E::mma(pa[ks2], make_uint4(v0.x, v0.y, v1.x, v1.y), o[db]);
       }
     }
-    if (tile + 1 < ntiles) {
-      store_tile(buf ^ 1);
-      if (tile + 2 < ntiles) load_tile(tile + 2);
-    }
-    __syncthreads();
   }
 
-  // Normalise and store: in block rb the lane holds rows 4*a + j, dims 16*db + lr.
+  // Normalise and store: lane holds rows 4*a + j, dims 16*db + lr.
+  const float l_row = xor32_sum(xor16_sum(l_run));
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float l_row = xor32_sum(xor16_sum(l_run[rb]));
+  for (int j = 0; j < 4; ++j) {
+    const float lj = from_lane(l_row, 4 * a + j);
+    const int row = r0 + wave * 16 + 4 * a + j;
+    if (row >= rows) continue;
+    const int t = row / G;
+    const int i = row % G;
+    uint16_t* orow = out + ((static_cast<size_t>(b) * n_head + g * G + i) * q_len + t) * D;
+    const float inv = lj > 0.0f ? 1.0f / lj : 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float lj = from_lane(l_row, 4 * a + j);
-      const int row = rw0 + 16 * rb + 4 * a + j;
-      if (row >= rows) continue;
-      const int t = row / G;
-      const int i = row % G;
-      uint16_t* orow = out + ((static_cast<size_t>(b) * n_head + g * G + i) * q_len + t) * D;
-      const float inv = lj > 0.0f ? 1.0f / lj : 0.0f;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) orow[16 * db + lr] = static_cast<uint16_t>(E::round(o[rb][db][j] * inv));
-    }
+    for (int db = 0; db < 8; ++db) orow[16 * db + lr] = static_cast<uint16_t>(E::round(o[db][j] * inv));
   }
 }
 
@@ -364,18 +324,12 @@ __global__ __launch_bounds__(256) void prefill_append_kernel(const uint4* __rest
   v_cache[dst] = v_new[static_cast<size_t>(row) * kChunks + c];
 }
 
-// One 16-row block per wavefront: two or four blocks per wavefront (each K and
-// V operand read from LDS feeding two or four MFMAs) measured no faster at
-// 4096-8192 tokens and slower for short prompts, at lower occupancy.
-constexpr int kPrefillRowBlocks = 1;
-
 template <class E, int G>
 hipError_t launch_prefill_g(const PrefillLaunch& p) {
-  constexpr int RB = kPrefillRowBlocks;
   const int rows = G * p.q_len;
-  const int row_tiles = (rows + 64 * RB - 1) / (64 * RB);
+  const int row_tiles = (rows + kRowsWG - 1) / kRowsWG;
   const int units = p.batch * p.n_kv_head;
-  hipLaunchKernelGGL((prefill_kernel<E, G, RB>), dim3(row_tiles * units), dim3(256), 0, p.stream,
+  hipLaunchKernelGGL((prefill_kernel<E, G>), dim3(row_tiles * units), dim3(256), 0, p.stream,
                      static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k_cache),
                      static_cast<const uint16_t*>(p.v_cache), p.start, static_cast<uint16_t*>(p.out), p.n_kv_head,
                      p.q_len, p.capacity, units, row_tiles, p.scale_log2);
