@@ -74,6 +74,11 @@ Plan forced_plan(int max_kv_len, int requested) {
 Plan heuristic_plan(int batch, int n_head, int n_kv_head, int max_kv_len, int num_cus) {
   if (batch <= 0 || n_head <= 0 || n_kv_head <= 0 || max_kv_len <= 0 || num_cus <= 0)
     return {1, max_kv_len > 0 ? max_kv_len : 1};
+  // A prefix of at most four 64-slot tiles: one workgroup per (row, KV head)
+  // streams it faster than a split call pays for its combine launch
+  // (measured on MI355X for 8-32 units at 235-256 slots).
+  if (max_kv_len <= 4 * ada::kTileRows)
+    return {1, static_cast<int>(ceil_div(max_kv_len, ada::kTileRows) * ada::kTileRows)};
   const int64_t units = static_cast<int64_t>(batch) * n_kv_head;
   const int64_t per_cu = n_head == n_kv_head ? 2 : 1;
   int64_t splits = ceil_div(per_cu * num_cus, units);

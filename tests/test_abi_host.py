@@ -254,7 +254,9 @@ def test_split_heuristic_properties(ada):
     assert ns(1, 16, 16, 1024, 256) == 16    # capped by 64-slot splits
     assert ns(4, 32, 8, 8192, 256) == 8      # MiniCPM shape: one workgroup per CU
     assert ns(1, 32, 8, 400, 256) == 7       # tiny
-    assert ns(1, 32, 8, 235, 256) == 4
+    assert ns(1, 32, 8, 235, 256) == 1       # at most 256 slots: one split, no combine launch
+    assert ns(1, 16, 16, 256, 256) == 1
+    assert ns(1, 16, 16, 257, 256) == 5
     for B in (1, 2, 4, 8, 16, 64):
         for Hq, Hkv in ((16, 16), (32, 8), (8, 1)):
             for n in (1, 63, 64, 65, 400, 1258, 4096, 8191, 32768, 131072, 1 << 20):
