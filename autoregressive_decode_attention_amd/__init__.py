@@ -12,6 +12,8 @@ The functions keep the C names without the ``ada_`` prefix:
 * ``decode_attn_gqa(q, k_cache, v_cache, kv_len, scale=None, out=None, max_kv_len=None)``
 * ``decode_attn_gqa_ex(..., num_splits=...)``
 * ``decode_step(q, k_new, v_new, k_cache, v_cache, pos, ...)``: append + decode in one call
+* ``step_graph(layers, pos, max_pos, ...)``: every layer's decode step plus the
+  position advance recorded once as a HIP graph (``StepGraph.launch()``)
 * ``decode_partial(q, k_cache, v_cache, kv_len, ...)`` and
   ``decode_combine(workspace, num_splits, out, n_kv_head)``: the two halves
 * ``decode_num_splits``, ``decode_workspace_bytes``, ``device_num_cus``,
@@ -39,7 +41,7 @@ MAX_SPLITS = 256
 STATUS = {
     0: "ADA_OK", -1: "ADA_ERR_NULL", -2: "ADA_ERR_SHAPE", -3: "ADA_ERR_GQA", -4: "ADA_ERR_DTYPE",
     -5: "ADA_ERR_HEAD_DIM", -6: "ADA_ERR_SCALE", -7: "ADA_ERR_WORKSPACE", -8: "ADA_ERR_SPLITS",
-    -9: "ADA_ERR_ALIGN", -10: "ADA_ERR_HIP",
+    -9: "ADA_ERR_ALIGN", -10: "ADA_ERR_HIP", -11: "ADA_ERR_DEVICE",
 }
 
 EXPORTS = (
@@ -47,8 +49,13 @@ EXPORTS = (
     "ada_kv_append", "ada_decode_num_splits", "ada_decode_workspace_bytes",
     "ada_decode_attn_gqa", "ada_decode_attn_gqa_ex", "ada_decode_partial", "ada_decode_combine",
     "ada_decode_step", "ada_rope_kv_append", "ada_decode_step_rope", "ada_prefill_append",
-    "ada_prefill_attn_gqa",
+    "ada_prefill_attn_gqa", "ada_step_graph_create", "ada_step_graph_launch", "ada_step_graph_destroy",
 )
+
+
+class StepLayer(ctypes.Structure):
+    """``ada_step_layer``: the buffers of one layer of a graph-captured step."""
+    _fields_ = [(name, ctypes.c_void_p) for name in ("q", "k_new", "v_new", "k_cache", "v_cache", "out", "cos", "sin")]
 
 
 class AdaError(RuntimeError):
@@ -88,6 +95,10 @@ def _declare(lib):
         "ada_prefill_attn_gqa": ([c_void_p] * 4 + [c_int] * 6 + [c_float, c_int, c_void_p, c_void_p], c_int),
         "ada_decode_step_rope": ([c_void_p] * 8 + [c_int] * 6 + [c_float, c_int, c_void_p, c_void_p, c_size_t,
                                                                  c_void_p, c_int], c_int),
+        "ada_step_graph_create": ([ctypes.POINTER(StepLayer), c_int, c_void_p] + [c_int] * 6 +
+                                  [c_float, c_int, c_int, c_void_p, c_size_t, ctypes.POINTER(c_void_p)], c_int),
+        "ada_step_graph_launch": ([c_void_p, c_void_p], c_int),
+        "ada_step_graph_destroy": ([c_void_p], None),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -504,6 +515,87 @@ def _decode_step(q, k_new, v_new, cos, sin, k_cache, v_cache, pos, scale, out, m
     return out
 
 
+class StepGraph:
+    """A whole multi-layer decode step recorded once as a HIP graph by
+    ``ada_step_graph_create``; ``launch()`` replays it on the current stream.
+    Holds references to every buffer it was built on, so they outlive it."""
+
+    def __init__(self, handle: int, device: torch.device, keep: tuple):
+        self._handle = handle
+        self.device = device
+        self._keep = keep
+
+    def launch(self) -> None:
+        _require(self._handle is not None, "step graph is closed")
+        _check(_lib.ada_step_graph_launch(ctypes.c_void_p(self._handle), ctypes.c_void_p(_stream(self.device))),
+               "ada_step_graph_launch")
+
+    def close(self) -> None:
+        """Free the graph; synchronise the streams it was launched on first."""
+        if self._handle is not None:
+            _lib.ada_step_graph_destroy(ctypes.c_void_p(self._handle))
+            self._handle = None
+            self._keep = ()
+
+    def __del__(self):
+        try:
+            if self._handle is not None:
+                torch.cuda.synchronize(self.device)
+            self.close()
+        except Exception:
+            pass
+
+
+def step_graph(layers, pos: torch.Tensor, max_pos: int, scale: float | None = None, advance: bool = True,
+               workspace: torch.Tensor | None = None) -> StepGraph:
+    """Record one decode step of every layer, in order, then the advance
+    pos[b] += 1 (when ``advance``), as one HIP graph.
+
+    ``layers``: a sequence of (q, k_new, v_new, k_cache, v_cache, out) or
+    (q, k_new, v_new, k_cache, v_cache, out, cos, sin) tuples, all layers with
+    the same cache shape and dtype; ``pos``: int32 GPU tensor [B];
+    ``max_pos``: the largest position any launch will see (sizes the
+    launches). Each launch of the returned graph runs ``decode_step`` (or
+    ``decode_step_rope``) on every layer with these buffers' current
+    contents."""
+    layers = list(layers)
+    _require(len(layers) > 0, "need at least one layer")
+    k0 = layers[0][3]
+    B, Hq, Hkv, S, D = _check_decode_inputs(layers[0][0], k0, layers[0][4])
+    dev = k0.device
+    pos_t = _as_int32(pos, B, dev)
+    _require(isinstance(pos, torch.Tensor), "pos must be an int32 GPU tensor (the graph advances it in place)")
+    structs = (StepLayer * len(layers))()
+    keep = [pos_t]
+    for i, layer in enumerate(layers):
+        _require(len(layer) in (6, 8), "a layer is (q, k_new, v_new, k_cache, v_cache, out[, cos, sin])")
+        q, k_new, v_new, kc, vc, out = layer[:6]
+        cos, sin = (layer[6], layer[7]) if len(layer) == 8 else (None, None)
+        _require(kc.shape == k0.shape and kc.dtype == k0.dtype and kc.device == dev,
+                 "every layer's caches must match the first layer's shape, dtype and device")
+        _check_decode_inputs(q, kc, vc)
+        for name, t in (("k_new", k_new), ("v_new", v_new)):
+            _require(t.dtype == kc.dtype and t.device == dev and t.is_contiguous() and t.numel() == B * Hkv * D,
+                     f"{name} must be a contiguous [B, Hkv, D] tensor like the cache")
+        _require(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous(), "out must be like q")
+        if cos is not None or sin is not None:
+            _check_tables(cos, sin, B, D, kc)
+        structs[i] = StepLayer(*(t.data_ptr() if t is not None else None for t in (q, k_new, v_new, kc, vc, out, cos, sin)))
+        keep.append(tuple(layer))
+    mp = int(max_pos)
+    splits = decode_num_splits(B, Hq, Hkv, min(mp + 1, S)) if 0 <= mp < S else 1
+    if workspace is None and splits > 1:
+        workspace = new_workspace(decode_workspace_bytes(B, Hq, Hkv, D, splits), dev)
+    keep.append(workspace)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    handle = ctypes.c_void_p(0)
+    _check(_lib.ada_step_graph_create(structs, len(layers), _ptr(pos_t), B, Hq, Hkv, D, S, mp, ctypes.c_float(scale),
+                                      _DTYPE_CODES[k0.dtype], 1 if advance else 0, _ptr(workspace), ws_bytes,
+                                      ctypes.byref(handle)), "ada_step_graph_create")
+    return StepGraph(handle.value, dev, tuple(keep))
+
+
 def decode_attn_gqa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len,
                     scale: float | None = None, out: torch.Tensor | None = None,
                     max_kv_len: int | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
@@ -522,5 +614,5 @@ __all__ = [
     "kv_append", "decode_attn_gqa", "decode_attn_gqa_ex", "decode_partial", "decode_combine", "decode_step", "decode_step_rope",
     "rope_kv_append", "prefill_append", "prefill_attn_gqa", "decode_num_splits", "decode_workspace_bytes",
     "new_workspace", "workspace_layout", "device_num_cus", "status_string", "last_hip_error",
-    "abi_version",
+    "abi_version", "StepGraph", "StepLayer", "step_graph",
 ]

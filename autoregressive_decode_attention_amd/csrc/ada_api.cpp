@@ -10,6 +10,7 @@
 #include <cmath>
 #include <climits>
 #include <cstdint>
+#include <vector>
 
 #include "ada_internal.h"
 
@@ -125,6 +126,7 @@ const char* ada_status_string(int status) {
     case ADA_ERR_SPLITS: return "num_splits out of range";
     case ADA_ERR_ALIGN: return "device pointers must be 16-byte aligned";
     case ADA_ERR_HIP: return "HIP runtime error (see ada_last_hip_error)";
+    case ADA_ERR_DEVICE: return "step graph launched on another device than the one it was created on";
     default: return "unknown status";
   }
 }
@@ -304,18 +306,32 @@ int ada_decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache,
 
 namespace {
 
-int decode_step_impl(const void* q, const void* k_new, const void* v_new, const void* cos, const void* sin,
-                     void* k_cache, void* v_cache, const int32_t* pos, int batch, int n_head, int n_kv_head,
-                     int head_dim, int capacity, int max_pos, float scale, int dtype, void* out,
-                     void* workspace, size_t workspace_bytes, void* stream, int num_splits) {
+// A validated decode step: the launch description and whether it uses the
+// balanced plan.
+struct StepLaunch {
+  ada::DecodeLaunch p;
+  bool balanced;
+};
+
+// Checks of a decode step (with rotary tables when cos/sin are given) and
+// its launch plan; nothing is enqueued. batch == 0 leaves s->p.batch == 0.
+int prepare_step(const void* q, const void* k_new, const void* v_new, const void* cos, const void* sin,
+                 void* k_cache, void* v_cache, const int32_t* pos, int batch, int n_head, int n_kv_head,
+                 int head_dim, int capacity, int max_pos, float scale, int dtype, void* out, void* workspace,
+                 size_t workspace_bytes, void* stream, int num_splits, StepLaunch* s) {
   if (max_pos < 0 || max_pos >= capacity) {
     if (dtype != ADA_F16 && dtype != ADA_BF16) return ADA_ERR_DTYPE;
     return ADA_ERR_SHAPE;
   }
-  ada::DecodeLaunch p{};
+  ada::DecodeLaunch& p = s->p;
+  s->balanced = false;
   int rc = prepare_decode(q, k_cache, v_cache, nullptr, batch, n_head, n_kv_head, head_dim, capacity,
                           max_pos + 1, scale, dtype, num_splits, stream, &p);
-  if (rc != ADA_OK || batch == 0) return rc;
+  if (rc != ADA_OK) return rc;
+  if (batch == 0) {
+    p.batch = 0;
+    return ADA_OK;
+  }
   if (!k_new || !v_new || !out) return ADA_ERR_NULL;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(out)) return ADA_ERR_ALIGN;
   if ((cos == nullptr) != (sin == nullptr)) return ADA_ERR_NULL;
@@ -332,18 +348,38 @@ int decode_step_impl(const void* q, const void* k_new, const void* v_new, const 
     if (rc != ADA_OK) return rc;
     p.workspace = workspace;
   }
-  const bool balanced = use_balanced(p, pos != nullptr, num_splits);
-  if (balanced) p.chunk = 0;
+  s->balanced = use_balanced(p, pos != nullptr, num_splits);
+  if (s->balanced) p.chunk = 0;
+  return ADA_OK;
+}
+
+// Enqueues a prepared step on `stream`: the partial kernel, then the combine
+// kernel when the step has more than one split.
+int launch_step(const StepLaunch& s, hipStream_t stream) {
+  ada::DecodeLaunch p = s.p;
+  if (p.batch == 0) return ADA_OK;
+  p.stream = stream;
   hipError_t e = ada::launch_partial(p);
   if (e != hipSuccess) return hip_fail(e);
   if (p.direct) return ADA_OK;
-  ada::CombineLaunch c{workspace, out, batch, n_head, n_kv_head, p.splits, dtype, p.stream};
-  c.balanced = balanced;
-  c.pos = pos;
+  ada::CombineLaunch c{p.workspace, p.out, p.batch, p.n_head, p.n_kv_head, p.splits, p.dtype, stream};
+  c.balanced = s.balanced;
+  c.pos = p.pos;
   c.step = true;
   c.max_kv_len = p.max_kv_len;
   e = ada::launch_combine(c);
   return e == hipSuccess ? ADA_OK : hip_fail(e);
+}
+
+int decode_step_impl(const void* q, const void* k_new, const void* v_new, const void* cos, const void* sin,
+                     void* k_cache, void* v_cache, const int32_t* pos, int batch, int n_head, int n_kv_head,
+                     int head_dim, int capacity, int max_pos, float scale, int dtype, void* out,
+                     void* workspace, size_t workspace_bytes, void* stream, int num_splits) {
+  StepLaunch s{};
+  int rc = prepare_step(q, k_new, v_new, cos, sin, k_cache, v_cache, pos, batch, n_head, n_kv_head, head_dim,
+                        capacity, max_pos, scale, dtype, out, workspace, workspace_bytes, stream, num_splits, &s);
+  if (rc != ADA_OK) return rc;
+  return launch_step(s, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -454,6 +490,110 @@ int ada_decode_combine(const void* workspace, size_t workspace_bytes, int batch,
                        static_cast<hipStream_t>(stream)};
   hipError_t e = ada::launch_combine(c);
   return e == hipSuccess ? ADA_OK : hip_fail(e);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Graph-captured multi-layer decode step.
+
+struct ada_step_graph {
+  hipGraphExec_t exec;  // NULL when the step has no work (batch 0)
+  int device;
+};
+
+namespace {
+
+// Records the prepared layers and the position advance on a private stream
+// and instantiates the graph.
+int capture_step(const std::vector<StepLaunch>& steps, int32_t* pos, int batch, int advance,
+                 hipGraphExec_t* exec) {
+  hipStream_t s = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+  if (e != hipSuccess) return hip_fail(e);
+  e = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(s);
+    return hip_fail(e);
+  }
+  int rc = ADA_OK;
+  for (const StepLaunch& st : steps) {
+    rc = launch_step(st, s);
+    if (rc != ADA_OK) break;
+  }
+  if (rc == ADA_OK && advance) {
+    e = ada::launch_advance_positions(pos, batch, 1, s);
+    if (e != hipSuccess) rc = hip_fail(e);
+  }
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(s, &graph);
+  if (rc == ADA_OK && e != hipSuccess) rc = hip_fail(e);
+  if (rc == ADA_OK) {
+    e = hipGraphInstantiate(exec, graph, nullptr, nullptr, 0);
+    if (e != hipSuccess) rc = hip_fail(e);
+  }
+  if (graph) (void)hipGraphDestroy(graph);
+  (void)hipStreamDestroy(s);
+  return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ada_step_graph_create(const ada_step_layer* layers, int n_layers, int32_t* pos, int batch, int n_head,
+                          int n_kv_head, int head_dim, int capacity, int max_pos, float scale, int dtype,
+                          int advance, void* workspace, size_t workspace_bytes, ada_step_graph** graph) {
+  if (!graph) return ADA_ERR_NULL;
+  *graph = nullptr;
+  if (n_layers <= 0) return ADA_ERR_SHAPE;
+  if (!layers) return ADA_ERR_NULL;
+  if (batch > 0 && !pos) return ADA_ERR_NULL;
+  if (pos && (reinterpret_cast<uintptr_t>(pos) & 3u) != 0) return ADA_ERR_ALIGN;
+  std::vector<StepLaunch> steps(static_cast<size_t>(n_layers));
+  // First every layer's arguments (a one-split plan needs no device query),
+  // then the real plans, which read the device's compute-unit count.
+  for (int i = 0; i < n_layers; ++i) {
+    const ada_step_layer& L = layers[i];
+    int rc = prepare_step(L.q, L.k_new, L.v_new, L.cos, L.sin, L.k_cache, L.v_cache, pos, batch, n_head,
+                          n_kv_head, head_dim, capacity, max_pos, scale, dtype, L.out, workspace, workspace_bytes,
+                          nullptr, 1, &steps[i]);
+    if (rc != ADA_OK) return rc;
+  }
+  for (int i = 0; i < n_layers; ++i) {
+    const ada_step_layer& L = layers[i];
+    int rc = prepare_step(L.q, L.k_new, L.v_new, L.cos, L.sin, L.k_cache, L.v_cache, pos, batch, n_head,
+                          n_kv_head, head_dim, capacity, max_pos, scale, dtype, L.out, workspace, workspace_bytes,
+                          nullptr, 0, &steps[i]);
+    if (rc != ADA_OK) return rc;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  hipGraphExec_t exec = nullptr;
+  if (batch > 0) {
+    int rc = capture_step(steps, pos, batch, advance, &exec);
+    if (rc != ADA_OK) return rc;
+  }
+  *graph = new ada_step_graph{exec, dev};
+  return ADA_OK;
+}
+
+int ada_step_graph_launch(ada_step_graph* graph, void* stream) {
+  if (!graph) return ADA_ERR_NULL;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev != graph->device) return ADA_ERR_DEVICE;
+  if (!graph->exec) return ADA_OK;
+  e = hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ADA_OK : hip_fail(e);
+}
+
+void ada_step_graph_destroy(ada_step_graph* graph) {
+  if (!graph) return;
+  if (graph->exec) (void)hipGraphExecDestroy(graph->exec);
+  delete graph;
 }
 
 }  // extern "C"

@@ -94,4 +94,6 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache,
                             const int32_t* pos, int batch, int n_kv_head, int capacity,
                             hipStream_t stream);
 
+hipError_t launch_advance_positions(int32_t* pos, int batch, int delta, hipStream_t stream);
+
 }  // namespace ada

@@ -250,8 +250,9 @@ def time_s2pro_run(ada, device) -> dict:
     """The S2-Pro-shaped run (36 layers, 32/8 heads, fp16, capacity 32768,
     prefill 234, then 1024 decode steps): one HIP graph holds a whole decode
     step -- per layer one ada_decode_step (append at slot 234 + i and attend
-    over 235 + i slots) -- plus a device-side increment of the position, so
-    one replay per step runs the whole run with no host work in between.
+    over 235 + i slots) -- plus the library's device-side increment of the
+    position (ada_step_graph_create), so one launch per step runs the whole
+    run with no host work in between.
     Timed over all 1024 replays (36 864 decode calls)."""
     wl = W.WORKLOADS["s2pro_run"]
     shp = wl.shape
@@ -275,27 +276,19 @@ def time_s2pro_run(ada, device) -> dict:
     ws = ada.new_workspace(ada.decode_workspace_bytes(B, Hq, Hkv, D, max(2, splits)), device)
     scale = 1.0 / math.sqrt(D)
 
-    def step():
-        for layer in range(L):
-            ada.decode_step(q[layer], k_new[layer], v_new[layer], kc[layer], vc[layer], pos, scale=scale,
-                            out=out[layer], max_pos=last - 1, workspace=ws)
-        pos.add_(1)
-
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        step()  # warm the binding outside capture
-    torch.cuda.current_stream().wait_stream(side)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        step()
+    # One library graph: every layer's ada_decode_step, then the position
+    # advance, recorded once (ada_step_graph_create) and replayed per step.
+    layers = [(q[layer], k_new[layer], v_new[layer], kc[layer], vc[layer], out[layer]) for layer in range(L)]
+    graph = ada.step_graph(layers, pos, last - 1, scale=scale, workspace=ws)
+    graph.launch()  # warm-up replay
     pos.fill_(T0)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(N):
-        g.replay()
+        graph.launch()
     torch.cuda.synchronize()
     run_ms = (time.perf_counter() - t0) * 1e3
+    graph.close()
     nbytes = L * sum(decode_bytes(B, Hq, Hkv, D, [n]) for n in range(T0 + 1, last + 1))
     del kc, vc
     return {"workload": "s2pro_run: 36 layers, 32/8 heads, head_dim 128, fp16, capacity 32768, prefill 234, "

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ADA_ABI_VERSION 1
+#define ADA_ABI_VERSION 2
 
 /* Element type of q, caches, new rows and output. */
 typedef enum ada_dtype { ADA_F16 = 0, ADA_BF16 = 1 } ada_dtype;
@@ -64,7 +64,9 @@ typedef enum ada_status {
   ADA_ERR_WORKSPACE = -7, /* workspace NULL or smaller than required          */
   ADA_ERR_SPLITS = -8,    /* num_splits outside [0, ADA_MAX_SPLITS]           */
   ADA_ERR_ALIGN = -9,     /* a device pointer is not 16-byte aligned          */
-  ADA_ERR_HIP = -10       /* a HIP runtime call failed                        */
+  ADA_ERR_HIP = -10,      /* a HIP runtime call failed                        */
+  ADA_ERR_DEVICE = -11    /* a step graph launched on another device than the
+                             one current when it was created                 */
 } ada_status;
 
 /* Upper bound on the number of key-range splits of one decode call. */
@@ -350,6 +352,83 @@ int ada_decode_partial(const void* q, const void* k_cache, const void* v_cache,
 int ada_decode_combine(const void* workspace, size_t workspace_bytes, int batch, int n_head,
                        int n_kv_head, int head_dim, int num_splits, int dtype, void* out,
                        void* stream);
+
+/*
+ * Graph-captured multi-layer decode step.
+ *
+ * Decode step i after a T-token prompt writes the new key/value rows at slot
+ * T + i and attends over T + i + 1 slots ([ACTIVE-PREFIX] section 2; section
+ * 4 of [FORWARD-STEP] does the same per layer with position_id). For a model
+ * with n_layers attention layers that share batch, head counts and cache
+ * capacity, ada_step_graph_create records, once, the launches of
+ * ada_decode_step (or ada_decode_step_rope for a layer with rotary tables)
+ * for every layer in order, followed by a kernel that adds one to every
+ * pos[b], into one HIP graph. Each ada_step_graph_launch then runs a whole
+ * step -- all layers and the position advance -- as a single graph launch
+ * with no host work and no device-to-host read: the positions live on the
+ * device and the kernels read them there.
+ *
+ * The graph holds the buffer addresses given at creation, not their
+ * contents: per step the caller writes the new q, k_new, v_new (and cos,
+ * sin) into the same buffers and reads out after the launch. Every layer
+ * uses the launch plan of ada_decode_step with the given max_pos (the split
+ * count for max_pos + 1 live slots on the device current at creation), so a
+ * replay gives bit for bit what those ada_decode_step calls would give.
+ *
+ *   layers    host array of n_layers (>= 1) layer descriptions, read only
+ *             during the call. Per layer: q [batch, n_head, head_dim],
+ *             k_new and v_new [batch, n_kv_head, head_dim], k_cache and
+ *             v_cache [batch, n_kv_head, capacity, head_dim], out
+ *             [batch, n_head, head_dim]; cos and sin [batch, head_dim] or
+ *             both NULL (no rotary embedding for that layer). Device
+ *             pointers, 16-byte aligned, with the no-overlap rules of
+ *             ada_decode_step.
+ *   pos       device int32 [batch], required: the slot each row appends at
+ *             in the next launch. A launch advances it by one when
+ *             `advance` is non-zero.
+ *   max_pos   host upper bound on pos[b] over every launch the caller will
+ *             make, 0 <= max_pos < capacity; sizes the launches. A row whose
+ *             pos[b] exceeds max_pos attends over max_pos + 1 slots only
+ *             (as in ada_decode_step).
+ *   workspace device scratch shared by the layers (they run in order), at
+ *             least ada_decode_workspace_bytes for the split count of
+ *             max_pos + 1 slots (may be NULL when that count is 1); it must
+ *             stay allocated, and untouched by other work that can overlap
+ *             a launch, for the life of the graph.
+ *   graph     receives the handle; set to NULL on any error.
+ * Other arguments as ada_decode_step. Every layer is validated before
+ * anything is recorded; an invalid layer returns its ada_decode_step status
+ * and creates nothing. Creation records on a private stream of its own and
+ * runs no kernel; it is ADA_ERR_HIP if graph capture or instantiation fails.
+ */
+typedef struct ada_step_layer {
+  const void* q;
+  const void* k_new;
+  const void* v_new;
+  void* k_cache;
+  void* v_cache;
+  void* out;
+  const void* cos; /* rotary tables for this layer, or NULL */
+  const void* sin;
+} ada_step_layer;
+
+typedef struct ada_step_graph ada_step_graph;
+
+int ada_step_graph_create(const ada_step_layer* layers, int n_layers, int32_t* pos, int batch, int n_head,
+                          int n_kv_head, int head_dim, int capacity, int max_pos, float scale, int dtype,
+                          int advance, void* workspace, size_t workspace_bytes, ada_step_graph** graph);
+
+/*
+ * One step: launches the graph on `stream` (ordered after earlier work on
+ * it, like any kernel launch). Launches of one graph share its workspace and
+ * positions and must be ordered. ADA_ERR_NULL for a NULL graph,
+ * ADA_ERR_DEVICE when the current device is not the one of its creation.
+ */
+int ada_step_graph_launch(ada_step_graph* graph, void* stream);
+
+/* Frees the graph (NULL is a no-op). No launch of it may still be pending:
+ * synchronise the streams it was launched on first. */
+void ada_step_graph_destroy(ada_step_graph* graph);
 
 #ifdef __cplusplus
 }

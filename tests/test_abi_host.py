@@ -47,8 +47,8 @@ def test_library_exports_every_declared_symbol(ada):
 
 
 def test_abi_version_and_status_strings(ada):
-    assert ada.abi_version() == 1
-    for code in range(-10, 1):
+    assert ada.abi_version() == 2
+    for code in range(-11, 1):
         assert ada.status_string(code) and ada.status_string(code) != "unknown status"
     assert ada.status_string(-99) == "unknown status"
 
@@ -167,6 +167,41 @@ def test_decode_step_validation(ada):
     assert f(*args(D=64)) == -5
     assert f(*args()) == -7                     # two splits need a workspace
     assert f(*args(splits=300)) == -8
+
+
+def test_step_graph_validation(ada):
+    """Host checks of the graph-captured step: every call here is rejected
+    before any HIP call, and the handle is left NULL."""
+    create = ada._lib.ada_step_graph_create
+    layer = lambda **kw: ada.StepLayer(*(kw.get(n, d) for n, d in (
+        ("q", 0x10000), ("k_new", 0x20000), ("v_new", 0x30000), ("k_cache", 0x40000), ("v_cache", 0x50000),
+        ("out", 0x60000), ("cos", None), ("sin", None))))
+
+    def call(layers=None, n=None, pos=P, B=1, D=128, S=2048, mp=399, dtype=0, scale=0.08, handle=True):
+        layers = layers if layers is not None else [layer(), layer()]
+        arr = (ada.StepLayer * max(len(layers), 1))(*layers)
+        h = ctypes.c_void_p(0xdead)
+        rc = create(arr, len(layers) if n is None else n, pos, B, 32, 8, D, S, mp, ctypes.c_float(scale), dtype, 1,
+                    NUL, 0, ctypes.byref(h) if handle else None)
+        if handle:
+            assert h.value is None, "the handle must be NULL after an error"
+        return rc
+
+    assert call(handle=False) == -1
+    assert call(n=0) == -2
+    assert call(pos=NUL) == -1
+    assert call(pos=ctypes.c_void_p(0x10002)) == -9
+    assert call(mp=2048) == -2
+    assert call(mp=-1) == -2
+    assert call(dtype=5) == -4
+    assert call(D=64) == -5
+    assert call(scale=float("inf")) == -6
+    assert call(layers=[layer(), layer(q=None)]) == -1          # the second layer is checked too
+    assert call(layers=[layer(k_cache=0x40008)]) == -9
+    assert create(None, 1, P, 1, 32, 8, 128, 2048, 399, ctypes.c_float(0.08), 0, 1, NUL, 0,
+                  ctypes.byref(ctypes.c_void_p())) == -1
+    assert ada._lib.ada_step_graph_launch(None, NUL) == -1
+    ada._lib.ada_step_graph_destroy(None)  # a no-op
 
 
 def test_rope_kv_append_validation(ada):
