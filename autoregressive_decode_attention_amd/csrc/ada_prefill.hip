@@ -23,14 +23,23 @@
 //   * S^T = K Q^T with v_mfma_f32_16x16x32 (16-bit inputs, fp32 sums): keys
 //     on M, query rows on N, head dims on K. A lane then holds, for one query
 //     row, 16 scores (4 keys in each of the tile's four 16-key blocks).
-//   * Online softmax in base 2 per row in fp32, exact running maximum; the
-//     weights are rounded once to the 16-bit type and the row sums use the
-//     rounded weights, so numerator and denominator see the same values.
+//   * Online softmax in base 2 per row in fp32 against a lazy reference: the
+//     output is rescaled only when a row's maximum passes its reference by
+//     more than 2^8, so the weights exp2(|scale| s - m) <= 256 need one FMA
+//     and one exp each. A negative scale is applied as |scale| to the
+//     negated query (an exact sign flip), which keeps the largest raw score
+//     the largest scaled one. The weights are rounded once to the 16-bit
+//     type, two per conversion, and the row sums add the rounded weights (a
+//     dot with ones), so numerator and denominator see the same values.
+//     Keys past a row's causal limit are masked only on the tiles that
+//     reach it.
 //   * O += P V with the same instruction: P is the A operand straight from
 //     registers, its K index running over the lane's 8 keys of a 32-key step
 //     (a fixed permutation of the keys, the same one the V operand uses).
-//     V is stored transposed in LDS ([dim][key]) so that each lane reads its
-//     8 keys of one dim as two 8-byte loads.
+//     V is stored transposed in LDS ([dim][key]) with each 32-key block in
+//     that operand order, so a lane reads its 8 keys of one dim as one
+//     16-byte load; the 144-byte row stride spreads a 16-lane read over all
+//     banks.
 //   * Row statistics move from the score layout (row = lane % 16) to the
 //     output layout (rows 4 * (lane / 16) + j) with ds_bpermute.
 //   * A tile is a fraction of a microsecond of matrix work while its loads
@@ -50,6 +59,9 @@ namespace {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bh2 __attribute__((ext_vector_type(2)));
 
 struct PF16 {
   static __device__ __forceinline__ f4 mma(const uint4& a, const uint4& b, f4 c) {
@@ -58,8 +70,13 @@ struct PF16 {
   static __device__ __forceinline__ uint32_t round(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
   }
-  static __device__ __forceinline__ float to_float(uint32_t bits) {
-    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+  // a and b rounded to nearest even, a in the low half.
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), h2));
+  }
+  // c plus both packed values (a dot with (1, 1): exact products, fp32 sum).
+  static __device__ __forceinline__ float sum2(uint32_t w, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), __builtin_bit_cast(h2, 0x3C003C00u), c, false);
   }
 };
 
@@ -70,14 +87,19 @@ struct PBF16 {
   static __device__ __forceinline__ uint32_t round(float x) {
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
   }
-  static __device__ __forceinline__ float to_float(uint32_t bits) { return __uint_as_float(bits << 16); }
+  static __device__ __forceinline__ uint32_t pack(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), bh2));
+  }
+  static __device__ __forceinline__ float sum2(uint32_t w, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bh2, w), __builtin_bit_cast(bh2, 0x3F803F80u), c, false);
+  }
 };
 
 constexpr int D = kHeadDim;     // 128
 constexpr int kRowsWG = 64;      // query rows per workgroup
 constexpr int kKeys = 64;        // key/value slots per tile
 constexpr int kKStride = D + 8;  // K tile row stride in LDS (u16): 272 B, 4-bank rotation per row
-constexpr int kVStride = 68;     // transposed V row stride (u16): 34 dwords, 2-bank rotation per row
+constexpr int kVStride = 72;     // transposed V row stride (u16): 144 B, 16-byte aligned rows
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float finite_ref(float m) { return m == kNegInf ? 0.0f : m; }
@@ -153,14 +175,25 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const uint16_t* __restr
   {
     const int i = my_row % G;
     const uint16_t* qrow = q + ((static_cast<size_t>(b) * n_head + g * G + i) * q_len + (row_ok ? my_t : 0)) * D;
+    // A negative scale is applied as |scale| to the negated query (a sign
+    // flip, exact), so the largest raw score is the largest scaled score.
+    const uint32_t sign = scale_log2 < 0.0f ? 0x80008000u : 0u;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qb[ks] = row_ok ? ld16(qrow + 32 * ks + 8 * a) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < 4; ++ks) {
+      uint4 v = row_ok ? ld16(qrow + 32 * ks + 8 * a) : make_uint4(0, 0, 0, 0);
+      qb[ks] = make_uint4(v.x ^ sign, v.y ^ sign, v.z ^ sign, v.w ^ sign);
+    }
   }
+  const float cscale = fabsf(scale_log2);
+  // Every key of a tile ending at or before this is visible to all of the
+  // wave's rows (rows past the prompt end are never stored).
+  const int wave_row0 = r0 + wave * 16;
+  const int wave_n_min = wave_row0 < rows ? visible(start, wave_row0 / G, capacity) : 0;
 
   f4 o[8];
 #pragma unroll
   for (int db = 0; db < 8; ++db) o[db] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = kNegInf;  // running max of row my_row (same in its 4 lanes)
+  float m_run = kNegInf;  // reference of row my_row (same in its 4 lanes), at most 8 below its max
   float l_run = 0.0f;     // this lane's share of the row's weight sum
 
   // Tile staging: K as 4 row chunks per thread (16 threads per 256-byte row),
@@ -196,13 +229,19 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const uint16_t* __restr
       const int c = tid / 32 + 8 * it;
       const uint32_t* r0w = reinterpret_cast<const uint32_t*>(&vreg[it][0]);
       const uint32_t* r1w = reinterpret_cast<const uint32_t*>(&vreg[it][1]);
+      // Keys are stored in operand order: within each 32-key block, the 8
+      // keys a lane group a reads (4a .. 4a + 3 and 16 + 4a .. 16 + 4a + 3)
+      // sit together at 8a .. 8a + 7, so one 16-byte read fetches them.
+      const int key = 2 * kp;
+      const int r = key % 32;
+      const int pos = (key - r) + 8 * ((r % 16) / 4) + 4 * (r / 16) + (r % 4);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         // dims 8c + 2w (low halves) and 8c + 2w + 1 (high halves) of keys 2kp, 2kp + 1
         const uint32_t lo = (r0w[w] & 0xffffu) | (r1w[w] << 16);
         const uint32_t hi = (r0w[w] >> 16) | (r1w[w] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(s_vt + (8 * c + 2 * w) * kVStride + 2 * kp) = lo;
-        *reinterpret_cast<uint32_t*>(s_vt + (8 * c + 2 * w + 1) * kVStride + 2 * kp) = hi;
+        *reinterpret_cast<uint32_t*>(s_vt + (8 * c + 2 * w) * kVStride + pos) = lo;
+        *reinterpret_cast<uint32_t*>(s_vt + (8 * c + 2 * w + 1) * kVStride + pos) = hi;
       }
     }
   };
@@ -226,27 +265,45 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const uint16_t* __restr
         s[nb] = E::mma(kop, qb[ks], s[nb]);
       }
     }
-    // Scale, mask (slots past the row's own position), tile maximum.
-    float x[4][4];
+    // Tile maximum of the raw scores (|scale| >= 0 keeps their order); keys
+    // past a row's own position are masked, on the tiles that reach them.
+    const bool full = base + kKeys <= wave_n_min;  // uniform across the wave
+    float sv[4][4];
+    bool ok[4][4];
     float mx = kNegInf;
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int key = base + 16 * nb + 4 * a + j;
-        x[nb][j] = key < my_n ? s[nb][j] * scale_log2 : kNegInf;
-        mx = fmaxf(mx, x[nb][j]);
+        ok[nb][j] = full || base + 16 * nb + 4 * a + j < my_n;
+        sv[nb][j] = ok[nb][j] ? s[nb][j] : kNegInf;
+        mx = fmaxf(mx, sv[nb][j]);
       }
     }
     mx = xor32_max(xor16_max(mx));  // over the row's 4 lanes
-    const float m_new = fmaxf(m_run, mx);
-    const float ref = finite_ref(m_new);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - ref);  // 0 while nothing was seen
-    m_run = m_new;
-    l_run *= alpha;
-    // Weights, rounded to the 16-bit type, packed as the A operand of P V:
-    // step ks2 holds keys base + 32*ks2 + 4*a + j (first half) and
-    // base + 32*ks2 + 16 + 4*a + j (second half), j = 0..3.
+    const float m_tile = mx == kNegInf ? kNegInf : mx * cscale;
+    // Lazy reference: rescale only when a row's maximum passes its reference
+    // by more than 2^8 (weights stay <= 256, exact in both 16-bit types).
+    const bool grow = m_tile > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? m_tile : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - finite_ref(m_new));  // 0 while nothing was seen
+      m_run = m_new;
+      l_run *= alpha;
+      float al[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) al[j] = from_lane(alpha, 4 * a + j);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[db][j] *= al[j];
+      }
+    }
+    const float nref = -finite_ref(m_run);
+    // Weights exp2(|scale| s - m), rounded to the 16-bit type, packed as the A
+    // operand of P V: step ks2 holds keys base + 32*ks2 + 4*a + j (first
+    // half) and base + 32*ks2 + 16 + 4*a + j (second half), j = 0..3. The
+    // row sum adds the rounded weights (a dot with ones, fp32).
     uint4 pa[2];
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
@@ -256,32 +313,25 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const uint16_t* __restr
         const int nb = 2 * ks2 + h;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-          const uint32_t p0 = E::round(__builtin_amdgcn_exp2f(x[nb][2 * jj] - ref));
-          const uint32_t p1 = E::round(__builtin_amdgcn_exp2f(x[nb][2 * jj + 1] - ref));
-          l_run += E::to_float(p0) + E::to_float(p1);
-          w[2 * h + jj] = p0 | (p1 << 16);
+          float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][2 * jj], cscale, nref));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][2 * jj + 1], cscale, nref));
+          if (!full) {
+            p0 = ok[nb][2 * jj] ? p0 : 0.0f;
+            p1 = ok[nb][2 * jj + 1] ? p1 : 0.0f;
+          }
+          w[2 * h + jj] = E::pack(p0, p1);
+          l_run = E::sum2(w[2 * h + jj], l_run);
         }
       }
       pa[ks2] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-    // Rescale the output rows this lane holds (rows 4*a + j of the wave).
-    float al[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) al[j] = from_lane(alpha, 4 * a + j);
-#pragma unroll
-    for (int db = 0; db < 8; ++db) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o[db][j] *= al[j];
     }
     // O += P V: B operand = V at the same 8 keys, dim 16*db + lr.
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const uint16_t* vrow = s_vt + (16 * db + lr) * kVStride + 32 * ks2 + 4 * a;
-        const uint2 v0 = *reinterpret_cast<const uint2*>(vrow);
-        const uint2 v1 = *reinterpret_cast<const uint2*>(vrow + 16);
-        o[db] = E::mma(pa[ks2], make_uint4(v0.x, v0.y, v1.x, v1.y), o[db]);
+        const uint4 vop = *reinterpret_cast<const uint4*>(s_vt + (16 * db + lr) * kVStride + 32 * ks2 + 8 * a);
+        o[db] = E::mma(pa[ks2], vop, o[db]);
       }
     }
   }
