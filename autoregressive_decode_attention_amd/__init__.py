@@ -49,7 +49,7 @@ EXPORTS = (
     "ada_kv_append", "ada_decode_num_splits", "ada_decode_workspace_bytes",
     "ada_decode_attn_gqa", "ada_decode_attn_gqa_ex", "ada_decode_partial", "ada_decode_combine",
     "ada_decode_step", "ada_rope_kv_append", "ada_decode_step_rope", "ada_prefill_append",
-    "ada_prefill_attn_gqa", "ada_step_graph_create", "ada_step_graph_launch", "ada_step_graph_destroy",
+    "ada_prefill_attn_gqa", "ada_prefill_rows_per_workgroup", "ada_step_graph_create", "ada_step_graph_launch", "ada_step_graph_destroy",
 )
 
 
@@ -98,6 +98,7 @@ def _declare(lib):
         "ada_step_graph_create": ([ctypes.POINTER(StepLayer), c_int, c_void_p] + [c_int] * 6 +
                                   [c_float, c_int, c_int, c_void_p, c_size_t, ctypes.POINTER(c_void_p)], c_int),
         "ada_step_graph_launch": ([c_void_p, c_void_p], c_int),
+        "ada_prefill_rows_per_workgroup": ([c_int] * 5, c_int),
         "ada_step_graph_destroy": ([c_void_p], None),
     }
     for name, (args, res) in sigs.items():
@@ -162,6 +163,13 @@ def decode_num_splits(batch: int, n_head: int, n_kv_head: int, max_kv_len: int, 
     if num_cus is None:
         num_cus = _cus(torch.device("cuda", torch.cuda.current_device()))
     return int(_lib.ada_decode_num_splits(int(batch), int(n_head), int(n_kv_head), int(max_kv_len), int(num_cus)))
+
+
+def prefill_rows_per_workgroup(batch: int, n_head: int, n_kv_head: int, q_len: int, num_cus: int | None = None) -> int:
+    """Query rows per workgroup prefill_attn_gqa uses (64 or 128) on a device
+    with ``num_cus`` compute units (default: the current device)."""
+    cus = device_num_cus() if num_cus is None else int(num_cus)
+    return int(_lib.ada_prefill_rows_per_workgroup(int(batch), int(n_head), int(n_kv_head), int(q_len), cus))
 
 
 def decode_workspace_bytes(batch: int, n_head: int, n_kv_head: int, head_dim: int, num_splits: int) -> int:
@@ -614,5 +622,5 @@ __all__ = [
     "kv_append", "decode_attn_gqa", "decode_attn_gqa_ex", "decode_partial", "decode_combine", "decode_step", "decode_step_rope",
     "rope_kv_append", "prefill_append", "prefill_attn_gqa", "decode_num_splits", "decode_workspace_bytes",
     "new_workspace", "workspace_layout", "device_num_cus", "status_string", "last_hip_error",
-    "abi_version", "StepGraph", "StepLayer", "step_graph",
+    "abi_version", "StepGraph", "StepLayer", "step_graph", "prefill_rows_per_workgroup",
 ]

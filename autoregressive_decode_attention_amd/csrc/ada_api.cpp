@@ -142,6 +142,10 @@ int ada_device_num_cus(int device, int* num_cus) {
   return ADA_OK;
 }
 
+int ada_prefill_rows_per_workgroup(int batch, int n_head, int n_kv_head, int q_len, int num_cus) {
+  return ada::prefill_rows_per_workgroup(batch, n_head, n_kv_head, q_len, num_cus);
+}
+
 int ada_decode_num_splits(int batch, int n_head, int n_kv_head, int max_kv_len, int num_cus) {
   return heuristic_plan(batch, n_head, n_kv_head, max_kv_len, num_cus).splits;
 }
@@ -449,6 +453,10 @@ int ada_prefill_attn_gqa(const void* q, const void* k_cache, const void* v_cache
   p.capacity = capacity;
   p.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   p.dtype = dtype;
+  int cus = 0;
+  int rc = current_device_cus(&cus);
+  if (rc != ADA_OK) return rc;
+  p.rows_per_workgroup = ada::prefill_rows_per_workgroup(batch, n_head, n_kv_head, q_len, cus);
   p.stream = static_cast<hipStream_t>(stream);
   hipError_t e = ada::launch_prefill(p);
   return e == hipSuccess ? ADA_OK : hip_fail(e);

@@ -74,8 +74,13 @@ struct PrefillLaunch {
   int batch, n_head, n_kv_head, q_len, capacity;
   float scale_log2;
   int dtype;
+  int rows_per_workgroup;  // 64 or 128, from prefill_rows_per_workgroup
   hipStream_t stream;
 };
+
+// Query rows per prefill workgroup (64 or 128) for a call on a device with
+// num_cus compute units; pure host arithmetic.
+int prefill_rows_per_workgroup(int batch, int n_head, int n_kv_head, int q_len, int num_cus);
 
 hipError_t launch_prefill(const PrefillLaunch& p);
 hipError_t launch_prefill_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

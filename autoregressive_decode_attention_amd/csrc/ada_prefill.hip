@@ -16,10 +16,11 @@
 // share every key and value row of their KV head, so the scores and the
 // weighted sum of values run on the matrix cores.
 //
-// Attention kernel, per workgroup: one (batch row, KV head) and 64 query
-// rows, where row r of the head group is token r / G and query head
+// Attention kernel, per workgroup: one (batch row, KV head) and 64 * RB
+// query rows, where row r of the head group is token r / G and query head
 // g*G + r % G (the G heads of a token share its causal limit). Four
-// wavefronts own 16 rows each. Key/value tiles of 64 slots go through LDS:
+// wavefronts own RB blocks of 16 rows each. Key/value tiles of 64 slots go
+// through LDS:
 //   * S^T = K Q^T with v_mfma_f32_16x16x32 (16-bit inputs, fp32 sums): keys
 //     on M, query rows on N, head dims on K. A lane then holds, for one query
 //     row, 16 scores (4 keys in each of the tile's four 16-key blocks).
@@ -42,12 +43,15 @@
 //     banks.
 //   * Row statistics move from the score layout (row = lane % 16) to the
 //     output layout (rows 4 * (lane / 16) + j) with ds_bpermute.
-//   * A tile is a fraction of a microsecond of matrix work while its loads
-//     (mostly L2 hits) take longer, so the kernel leans on occupancy to
-//     overlap them: one 35 KB LDS tile per workgroup (loaded into registers
-//     one tile ahead, two barriers per tile) and registers capped for three
-//     wavefronts per SIMD. Measured on MI355X this beat double-buffered LDS
-//     at two per SIMD by 14 % (4096-8192-token prompts); four per SIMD spill.
+//   * LDS traffic is what bounds the kernel (on MI355X, removing the LDS
+//     operand reads and staging stores made it 44 % faster, removing either
+//     matrix product or the softmax 7-12 %): each tile is staged once into
+//     one 35 KB LDS buffer (loaded into registers one tile ahead, two
+//     barriers per tile) and read by all four wavefronts. With RB = 2 each K
+//     and V operand read serves two row blocks, halving the LDS bytes per
+//     matrix instruction, at two wavefronts per SIMD; RB = 1 keeps three per
+//     SIMD for launches too small to fill the device with 128-row
+//     workgroups (prefill_rows_per_workgroup decides).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -96,7 +100,6 @@ struct PBF16 {
 };
 
 constexpr int D = kHeadDim;     // 128
-constexpr int kRowsWG = 64;      // query rows per workgroup
 constexpr int kKeys = 64;        // key/value slots per tile
 constexpr int kKStride = D + 8;  // K tile row stride in LDS (u16): 272 B, 4-bank rotation per row
 constexpr int kVStride = 72;     // transposed V row stride (u16): 144 B, 16-byte aligned rows
@@ -133,13 +136,14 @@ __device__ __forceinline__ int visible(int start, int t, int capacity) {
   return n < 0 ? 0 : (n > capacity ? capacity : static_cast<int>(n));
 }
 
-template <class E, int G>
-__global__ __launch_bounds__(256, 3) void prefill_kernel(const uint16_t* __restrict__ q,
+template <class E, int G, int RB>
+__global__ __launch_bounds__(256, RB == 1 ? 3 : 2) void prefill_kernel(const uint16_t* __restrict__ q,
                                                       const uint16_t* __restrict__ k_cache,
                                                       const uint16_t* __restrict__ v_cache,
                                                       const int32_t* __restrict__ start_arr,
                                                       uint16_t* __restrict__ out, int n_kv_head, int q_len,
                                                       int capacity, int units, int row_tiles, float scale_log2) {
+  constexpr int kRows = 64 * RB;  // query rows per workgroup: RB blocks of 16 per wave
   __shared__ __align__(16) uint16_t s_k[kKeys * kKStride];
   __shared__ __align__(16) uint16_t s_vt[D * kVStride];
 
@@ -157,8 +161,8 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const uint16_t* __restr
   const int n_head = n_kv_head * G;
   const int rows = G * q_len;
   const int start = start_arr != nullptr ? start_arr[b] : 0;
-  const int r0 = rt * kRowsWG;
-  const int t_last = min(q_len - 1, (min(r0 + kRowsWG, rows) - 1) / G);
+  const int r0 = rt * kRows;
+  const int t_last = min(q_len - 1, (min(r0 + kRows, rows) - 1) / G);
   const int n_max = visible(start, t_last, capacity);
   const int ntiles = (n_max + kKeys - 1) / kKeys;
 
@@ -166,35 +170,42 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const uint16_t* __restr
   const uint16_t* kbase = k_cache + head_off;
   const uint16_t* vbase = v_cache + head_off;
 
-  // This lane's query row in the score layout (row lr of the wave's 16).
-  const int my_row = r0 + wave * 16 + lr;
-  const int my_t = my_row / G;
-  const bool row_ok = my_row < rows;
-  const int my_n = row_ok ? visible(start, my_t, capacity) : 0;
-  uint4 qb[4];  // Q^T operand: dims 32*ks + 8*a .. + 8 of row my_row
-  {
+  // Row block rb of this wave: rows wave_row0 + 16 rb .. + 15; this lane's
+  // query row in the score layout is row lr of each block.
+  const int wave_row0 = r0 + wave * 16 * RB;
+  const float cscale = fabsf(scale_log2);
+  // A negative scale is applied as |scale| to the negated query (a sign
+  // flip, exact), so the largest raw score is the largest scaled score.
+  const uint32_t sign = scale_log2 < 0.0f ? 0x80008000u : 0u;
+  int my_n[RB];
+  uint4 qb[RB][4];  // Q^T operand: dims 32*ks + 8*a .. + 8 of the block's row lr
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int my_row = wave_row0 + 16 * rb + lr;
+    const int my_t = my_row / G;
+    const bool row_ok = my_row < rows;
+    my_n[rb] = row_ok ? visible(start, my_t, capacity) : 0;
     const int i = my_row % G;
     const uint16_t* qrow = q + ((static_cast<size_t>(b) * n_head + g * G + i) * q_len + (row_ok ? my_t : 0)) * D;
-    // A negative scale is applied as |scale| to the negated query (a sign
-    // flip, exact), so the largest raw score is the largest scaled score.
-    const uint32_t sign = scale_log2 < 0.0f ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       uint4 v = row_ok ? ld16(qrow + 32 * ks + 8 * a) : make_uint4(0, 0, 0, 0);
-      qb[ks] = make_uint4(v.x ^ sign, v.y ^ sign, v.z ^ sign, v.w ^ sign);
+      qb[rb][ks] = make_uint4(v.x ^ sign, v.y ^ sign, v.z ^ sign, v.w ^ sign);
     }
   }
-  const float cscale = fabsf(scale_log2);
   // Every key of a tile ending at or before this is visible to all of the
   // wave's rows (rows past the prompt end are never stored).
-  const int wave_row0 = r0 + wave * 16;
   const int wave_n_min = wave_row0 < rows ? visible(start, wave_row0 / G, capacity) : 0;
 
-  f4 o[8];
+  f4 o[RB][8];
+  float m_run[RB], l_run[RB];  // per block: row reference (at most 8 below its max), this lane's weight sum
 #pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-  float m_run = kNegInf;  // reference of row my_row (same in its 4 lanes), at most 8 below its max
-  float l_run = 0.0f;     // this lane's share of the row's weight sum
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[rb][db] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    m_run[rb] = kNegInf;
+    l_run[rb] = 0.0f;
+  }
 
   // Tile staging: K as 4 row chunks per thread (16 threads per 256-byte row),
   // V as two rows x one 16-byte chunk (key pair kp, dims 8c .. 8c + 8) twice.
@@ -254,101 +265,112 @@ __global__ __launch_bounds__(256, 3) void prefill_kernel(const uint16_t* __restr
     if (tile + 1 < ntiles) load_tile(tile + 1);
     const int base = tile * kKeys;
 
-    // S^T = K Q^T: block nb holds keys base + 16*nb + 4*a + j for row my_row.
-    f4 s[4];
+    // S^T = K Q^T: block nb holds keys base + 16*nb + 4*a + j for the row;
+    // each K operand read serves every row block.
+    f4 s[RB][4];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) s[rb][nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
-      s[nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const uint4 kop = *reinterpret_cast<const uint4*>(s_k + (16 * nb + lr) * kKStride + 32 * ks + 8 * a);
-        s[nb] = E::mma(kop, qb[ks], s[nb]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) s[rb][nb] = E::mma(kop, qb[rb][ks], s[rb][nb]);
       }
     }
-    // Tile maximum of the raw scores (|scale| >= 0 keeps their order); keys
-    // past a row's own position are masked, on the tiles that reach them.
     const bool full = base + kKeys <= wave_n_min;  // uniform across the wave
-    float sv[4][4];
-    bool ok[4][4];
-    float mx = kNegInf;
+    uint4 pa[RB][2];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int rb = 0; rb < RB; ++rb) {
+      // Tile maximum of the raw scores (|scale| >= 0 keeps their order); keys
+      // past a row's own position are masked, on the tiles that reach them.
+      bool ok[4][4];
+      float mx = kNegInf;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        ok[nb][j] = full || base + 16 * nb + 4 * a + j < my_n;
-        sv[nb][j] = ok[nb][j] ? s[nb][j] : kNegInf;
-        mx = fmaxf(mx, sv[nb][j]);
-      }
-    }
-    mx = xor32_max(xor16_max(mx));  // over the row's 4 lanes
-    const float m_tile = mx == kNegInf ? kNegInf : mx * cscale;
-    // Lazy reference: rescale only when a row's maximum passes its reference
-    // by more than 2^8 (weights stay <= 256, exact in both 16-bit types).
-    const bool grow = m_tile > m_run + 8.0f;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = grow ? m_tile : m_run;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - finite_ref(m_new));  // 0 while nothing was seen
-      m_run = m_new;
-      l_run *= alpha;
-      float al[4];
+      for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) al[j] = from_lane(alpha, 4 * a + j);
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o[db][j] *= al[j];
-      }
-    }
-    const float nref = -finite_ref(m_run);
-    // Weights exp2(|scale| s - m), rounded to the 16-bit type, packed as the A
-    // operand of P V: step ks2 holds keys base + 32*ks2 + 4*a + j (first
-    // half) and base + 32*ks2 + 16 + 4*a + j (second half), j = 0..3. The
-    // row sum adds the rounded weights (a dot with ones, fp32).
-    uint4 pa[2];
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      uint32_t w[4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int nb = 2 * ks2 + h;
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][2 * jj], cscale, nref));
-          float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][2 * jj + 1], cscale, nref));
-          if (!full) {
-            p0 = ok[nb][2 * jj] ? p0 : 0.0f;
-            p1 = ok[nb][2 * jj + 1] ? p1 : 0.0f;
-          }
-          w[2 * h + jj] = E::pack(p0, p1);
-          l_run = E::sum2(w[2 * h + jj], l_run);
+        for (int j = 0; j < 4; ++j) {
+          ok[nb][j] = full || base + 16 * nb + 4 * a + j < my_n[rb];
+          mx = fmaxf(mx, ok[nb][j] ? s[rb][nb][j] : kNegInf);
         }
       }
-      pa[ks2] = make_uint4(w[0], w[1], w[2], w[3]);
+      mx = xor32_max(xor16_max(mx));  // over the row's 4 lanes
+      const float m_tile = mx == kNegInf ? kNegInf : mx * cscale;
+      // Lazy reference: rescale only when a row's maximum passes its
+      // reference by more than 2^8 (weights stay <= 256).
+      const bool grow = m_tile > m_run[rb] + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? m_tile : m_run[rb];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - finite_ref(m_new));  // 0 while nothing was seen
+        m_run[rb] = m_new;
+        l_run[rb] *= alpha;
+        float al[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) al[j] = from_lane(alpha, 4 * a + j);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[rb][db][j] *= al[j];
+        }
+      }
+      const float nref = -finite_ref(m_run[rb]);
+      // Weights exp2(|scale| s - m), rounded to the 16-bit type, packed as the
+      // A operand of P V: step ks2 holds keys base + 32*ks2 + 4*a + j (first
+      // half) and base + 32*ks2 + 16 + 4*a + j (second half), j = 0..3. The
+      // row sum adds the rounded weights (a dot with ones, fp32).
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        uint32_t w[4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int nb = 2 * ks2 + h;
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) {
+            float p0 = __builtin_amdgcn_exp2f(fmaf(s[rb][nb][2 * jj], cscale, nref));
+            float p1 = __builtin_amdgcn_exp2f(fmaf(s[rb][nb][2 * jj + 1], cscale, nref));
+            if (!full) {
+              p0 = ok[nb][2 * jj] ? p0 : 0.0f;
+              p1 = ok[nb][2 * jj + 1] ? p1 : 0.0f;
+            }
+            w[2 * h + jj] = E::pack(p0, p1);
+            l_run[rb] = E::sum2(w[2 * h + jj], l_run[rb]);
+          }
+        }
+        pa[rb][ks2] = make_uint4(w[0], w[1], w[2], w[3]);
+      }
     }
-    // O += P V: B operand = V at the same 8 keys, dim 16*db + lr.
+    // O += P V: B operand = V at the same 8 keys, dim 16*db + lr; each V
+    // operand read serves every row block.
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
         const uint4 vop = *reinterpret_cast<const uint4*>(s_vt + (16 * db + lr) * kVStride + 32 * ks2 + 8 * a);
-        o[db] = E::mma(pa[ks2], vop, o[db]);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) o[rb][db] = E::mma(pa[rb][ks2], vop, o[rb][db]);
       }
     }
   }
 
-  // Normalise and store: lane holds rows 4*a + j, dims 16*db + lr.
-  const float l_row = xor32_sum(xor16_sum(l_run));
+  // Normalise and store: lane holds rows 4*a + j of each block, dims 16*db + lr.
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float lj = from_lane(l_row, 4 * a + j);
-    const int row = r0 + wave * 16 + 4 * a + j;
-    if (row >= rows) continue;
-    const int t = row / G;
-    const int i = row % G;
-    uint16_t* orow = out + ((static_cast<size_t>(b) * n_head + g * G + i) * q_len + t) * D;
-    const float inv = lj > 0.0f ? 1.0f / lj : 0.0f;
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l_row = xor32_sum(xor16_sum(l_run[rb]));
 #pragma unroll
-    for (int db = 0; db < 8; ++db) orow[16 * db + lr] = static_cast<uint16_t>(E::round(o[db][j] * inv));
+    for (int j = 0; j < 4; ++j) {
+      const float lj = from_lane(l_row, 4 * a + j);
+      const int row = wave_row0 + 16 * rb + 4 * a + j;
+      if (row >= rows) continue;
+      const int t = row / G;
+      const int i = row % G;
+      uint16_t* orow = out + ((static_cast<size_t>(b) * n_head + g * G + i) * q_len + t) * D;
+      const float inv = lj > 0.0f ? 1.0f / lj : 0.0f;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) orow[16 * db + lr] = static_cast<uint16_t>(E::round(o[rb][db][j] * inv));
+    }
   }
 }
 
@@ -374,16 +396,21 @@ __global__ __launch_bounds__(256) void prefill_append_kernel(const uint4* __rest
   v_cache[dst] = v_new[static_cast<size_t>(row) * kChunks + c];
 }
 
-template <class E, int G>
-hipError_t launch_prefill_g(const PrefillLaunch& p) {
+template <class E, int G, int RB>
+hipError_t launch_prefill_rb(const PrefillLaunch& p) {
   const int rows = G * p.q_len;
-  const int row_tiles = (rows + kRowsWG - 1) / kRowsWG;
+  const int row_tiles = (rows + 64 * RB - 1) / (64 * RB);
   const int units = p.batch * p.n_kv_head;
-  hipLaunchKernelGGL((prefill_kernel<E, G>), dim3(row_tiles * units), dim3(256), 0, p.stream,
+  hipLaunchKernelGGL((prefill_kernel<E, G, RB>), dim3(row_tiles * units), dim3(256), 0, p.stream,
                      static_cast<const uint16_t*>(p.q), static_cast<const uint16_t*>(p.k_cache),
                      static_cast<const uint16_t*>(p.v_cache), p.start, static_cast<uint16_t*>(p.out), p.n_kv_head,
                      p.q_len, p.capacity, units, row_tiles, p.scale_log2);
   return hipGetLastError();
+}
+
+template <class E, int G>
+hipError_t launch_prefill_g(const PrefillLaunch& p) {
+  return p.rows_per_workgroup == 128 ? launch_prefill_rb<E, G, 2>(p) : launch_prefill_rb<E, G, 1>(p);
 }
 
 template <class E>
@@ -402,6 +429,20 @@ hipError_t launch_prefill_e(const PrefillLaunch& p) {
 }
 
 }  // namespace
+
+// Two 16-row blocks per wavefront halve the LDS traffic per matrix
+// instruction (each K and V operand read serves both blocks) but halve the
+// workgroup count and allow two waves per SIMD instead of three, so they pay
+// only when the launch still has at least four workgroups per compute unit
+// (measured on MI355X: 15-18 % faster at 4096-8192-token 32/8 prompts, 20 %
+// slower at 1024 tokens, where one workgroup per unit would remain).
+int prefill_rows_per_workgroup(int batch, int n_head, int n_kv_head, int q_len, int num_cus) {
+  if (batch <= 0 || n_head <= 0 || n_kv_head <= 0 || q_len <= 0 || num_cus <= 0 || n_head % n_kv_head != 0)
+    return 64;
+  const long rows = static_cast<long>(n_head / n_kv_head) * q_len;
+  const long workgroups = (rows + 127) / 128 * batch * n_kv_head;
+  return workgroups >= 4L * num_cus ? 128 : 64;
+}
 
 hipError_t launch_prefill(const PrefillLaunch& p) {
   return p.dtype == 1 ? launch_prefill_e<PBF16>(p) : launch_prefill_e<PF16>(p);

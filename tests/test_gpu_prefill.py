@@ -122,6 +122,19 @@ def test_prefill_long_prompt(ada, ora):
     run_prefill(ada, ora, 1, 32, 8, 1024, 2048, "bf16", [0], 840, "long prompt")
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_prefill_two_row_blocks(ada, ora, dtype):
+    """Launches large enough for 128-row workgroups (two 16-row blocks per
+    wavefront, every K and V operand read serving both): the rule picks them
+    on this device, and the results match the oracle with ragged starts and
+    with a last row tile whose upper two wavefronts hold no row."""
+    cases = [(16, 32, 8, 256, 600, [0, 7, 100, 333, 0, 1, 64, 200, 5, 9, 300, 17, 0, 250, 128, 40]),  # G = 4
+             (32, 64, 8, 72, 200, [3 * i for i in range(32)])]  # G = 8: 576 rows, last tile 64 of 128
+    for k, (B, Hq, Hkv, T, S, starts) in enumerate(cases):
+        assert ada.prefill_rows_per_workgroup(B, Hq, Hkv, T) == 128, "this case must take the two-block path"
+        run_prefill(ada, ora, B, Hq, Hkv, T, S, dtype, starts, 880 + k, f"two row blocks {k}")
+
+
 def test_prefill_rows_match_decode(ada):
     """Token t of the prefill attends what a one-token decode with
     kv_len = start + t + 1 attends: the two kernels agree within the tolerance."""
