@@ -37,17 +37,21 @@
 //   * O += P V with the same instruction: P is the A operand straight from
 //     registers, its K index running over the lane's 8 keys of a 32-key step
 //     (a fixed permutation of the keys, the same one the V operand uses).
-//     V is stored transposed in LDS ([dim][key]) with each 32-key block in
-//     that operand order, so a lane reads its 8 keys of one dim as one
-//     16-byte load; the 144-byte row stride spreads a 16-lane read over all
+//     V is staged row-major like K and read with the transposing LDS read
+//     (ds_read_b64_tr_b16): within each 16-lane group, lane s addresses key
+//     row r + s / 4 at dims 4 * (s % 4) .. + 3 of a 16-dim block, and lane d
+//     receives keys r .. r + 3 of dim d of that block (the layout was
+//     measured with a probe on MI355X). Two such reads give a lane its 8
+//     keys; the 288-byte V row stride puts the 4 rows of a read in disjoint
 //     banks.
 //   * Row statistics move from the score layout (row = lane % 16) to the
 //     output layout (rows 4 * (lane / 16) + j) with ds_bpermute.
 //   * LDS traffic is what bounds the kernel (on MI355X, removing the LDS
 //     operand reads and staging stores made it 44 % faster, removing either
 //     matrix product or the softmax 7-12 %): each tile is staged once into
-//     one 35 KB LDS buffer (loaded into registers one tile ahead, two
-//     barriers per tile) and read by all four wavefronts. With RB = 2 each K
+//     one 35 KB LDS buffer (loaded into registers one tile ahead, stored
+//     with 16-byte writes, two barriers per tile) and read by all four
+//     wavefronts. With RB = 2 each K
 //     and V operand read serves two row blocks, halving the LDS bytes per
 //     matrix instruction, at two wavefronts per SIMD; RB = 1 keeps three per
 //     SIMD for launches too small to fill the device with 128-row
@@ -66,6 +70,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bh2 __attribute__((ext_vector_type(2)));
+typedef short s4 __attribute__((ext_vector_type(4)));
 
 struct PF16 {
   static __device__ __forceinline__ f4 mma(const uint4& a, const uint4& b, f4 c) {
@@ -102,7 +107,7 @@ struct PBF16 {
 constexpr int D = kHeadDim;     // 128
 constexpr int kKeys = 64;        // key/value slots per tile
 constexpr int kKStride = D + 8;  // K tile row stride in LDS (u16): 272 B, 4-bank rotation per row
-constexpr int kVStride = 72;     // transposed V row stride (u16): 144 B, 16-byte aligned rows
+constexpr int kVStride = D + 16; // V row stride (u16): 288 B, so the 4 rows of a transposing read hit disjoint banks
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float finite_ref(float m) { return m == kNegInf ? 0.0f : m; }
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(256, RB == 1 ? 3 : 2) void prefill_kernel(const uin
                                                       int capacity, int units, int row_tiles, float scale_log2) {
   constexpr int kRows = 64 * RB;  // query rows per workgroup: RB blocks of 16 per wave
   __shared__ __align__(16) uint16_t s_k[kKeys * kKStride];
-  __shared__ __align__(16) uint16_t s_vt[D * kVStride];
+  __shared__ __align__(16) uint16_t s_v[kKeys * kVStride];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -207,25 +212,17 @@ __global__ __launch_bounds__(256, RB == 1 ? 3 : 2) void prefill_kernel(const uin
     l_run[rb] = 0.0f;
   }
 
-  // Tile staging: K as 4 row chunks per thread (16 threads per 256-byte row),
-  // V as two rows x one 16-byte chunk (key pair kp, dims 8c .. 8c + 8) twice.
-  uint4 kreg[4], vreg[2][2];
+  // Tile staging: K and V row-major, 4 row chunks per thread each (16
+  // threads per 256-byte row).
+  uint4 kreg[4], vreg[4];
   auto load_tile = [&](int tile) {
     const int base = tile * kKeys;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int idx = tid + 256 * it;
-      const int key = min(base + idx / 16, n_max - 1);
-      kreg[it] = ld16(kbase + static_cast<size_t>(key) * D + 8 * (idx % 16));
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int kp = tid % 32;
-      const int c = tid / 32 + 8 * it;
-      const int k0 = min(base + 2 * kp, n_max - 1);
-      const int k1 = min(base + 2 * kp + 1, n_max - 1);
-      vreg[it][0] = ld16(vbase + static_cast<size_t>(k0) * D + 8 * c);
-      vreg[it][1] = ld16(vbase + static_cast<size_t>(k1) * D + 8 * c);
+      const size_t off = static_cast<size_t>(min(base + idx / 16, n_max - 1)) * D + 8 * (idx % 16);
+      kreg[it] = ld16(kbase + off);
+      vreg[it] = ld16(vbase + off);
     }
   };
   auto store_tile = [&]() {
@@ -233,27 +230,7 @@ __global__ __launch_bounds__(256, RB == 1 ? 3 : 2) void prefill_kernel(const uin
     for (int it = 0; it < 4; ++it) {
       const int idx = tid + 256 * it;
       *reinterpret_cast<uint4*>(s_k + (idx / 16) * kKStride + 8 * (idx % 16)) = kreg[it];
-    }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int kp = tid % 32;
-      const int c = tid / 32 + 8 * it;
-      const uint32_t* r0w = reinterpret_cast<const uint32_t*>(&vreg[it][0]);
-      const uint32_t* r1w = reinterpret_cast<const uint32_t*>(&vreg[it][1]);
-      // Keys are stored in operand order: within each 32-key block, the 8
-      // keys a lane group a reads (4a .. 4a + 3 and 16 + 4a .. 16 + 4a + 3)
-      // sit together at 8a .. 8a + 7, so one 16-byte read fetches them.
-      const int key = 2 * kp;
-      const int r = key % 32;
-      const int pos = (key - r) + 8 * ((r % 16) / 4) + 4 * (r / 16) + (r % 4);
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // dims 8c + 2w (low halves) and 8c + 2w + 1 (high halves) of keys 2kp, 2kp + 1
-        const uint32_t lo = (r0w[w] & 0xffffu) | (r1w[w] << 16);
-        const uint32_t hi = (r0w[w] >> 16) | (r1w[w] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(s_vt + (8 * c + 2 * w) * kVStride + pos) = lo;
-        *reinterpret_cast<uint32_t*>(s_vt + (8 * c + 2 * w + 1) * kVStride + pos) = hi;
-      }
+      *reinterpret_cast<uint4*>(s_v + (idx / 16) * kVStride + 8 * (idx % 16)) = vreg[it];
     }
   };
 
@@ -348,7 +325,16 @@ __global__ __launch_bounds__(256, RB == 1 ? 3 : 2) void prefill_kernel(const uin
     for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const uint4 vop = *reinterpret_cast<const uint4*>(s_vt + (16 * db + lr) * kVStride + 32 * ks2 + 8 * a);
+        // Two transposing reads: within each 16-lane group, lane s points at
+        // key row r + s / 4, dims 16*db + 4*(s % 4) .. + 3, and lane d
+        // receives keys r .. r + 3 of dim 16*db + d (r = 32*ks2 + 4*a, then
+        // r + 16): the operand's 8 keys in the order the weights use.
+        const uint16_t* vp = s_v + (32 * ks2 + 4 * a + (lr >> 2)) * kVStride + 16 * db + 4 * (lr & 3);
+        const s4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(vp));
+        const s4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(vp + 16 * kVStride));
+        const uint2 w0 = __builtin_bit_cast(uint2, v0);
+        const uint2 w1 = __builtin_bit_cast(uint2, v1);
+        const uint4 vop = make_uint4(w0.x, w0.y, w1.x, w1.y);
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) o[rb][db] = E::mma(pa[rb][ks2], vop, o[rb][db]);
       }
