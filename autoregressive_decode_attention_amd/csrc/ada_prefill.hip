@@ -21,6 +21,16 @@
 // g*G + r % G (the G heads of a token share its causal limit). Four
 // wavefronts own RB blocks of 16 rows each. Key/value tiles of 64 slots go
 // through LDS:
+//   * Staging: direct-to-LDS loads (global_load_lds_dwordx4) carry each K
+//     and V tile from memory into one of two LDS buffers with no staging
+//     registers and no LDS store instructions; the next tile's loads are in
+//     flight while this tile is computed, and one barrier per tile both
+//     publishes the next tile and frees the current buffer. Such a load
+//     writes a wave's 64 x 16 bytes contiguously in lane order, so rows
+//     cannot be padded: row R keeps its 16-byte chunk c in slot c ^ swz(R)
+//     instead, which makes the K operand reads and the transposing V reads
+//     below bank-conflict-free (each lane loads the chunk that belongs in
+//     its slot, so every 16 lanes still read one whole 256-byte row).
 //   * S^T = K Q^T with v_mfma_f32_16x16x32 (16-bit inputs, fp32 sums): keys
 //     on M, query rows on N, head dims on K. A lane then holds, for one query
 //     row, 16 scores (4 keys in each of the tile's four 16-key blocks).
@@ -37,25 +47,20 @@
 //   * O += P V with the same instruction: P is the A operand straight from
 //     registers, its K index running over the lane's 8 keys of a 32-key step
 //     (a fixed permutation of the keys, the same one the V operand uses).
-//     V is staged row-major like K and read with the transposing LDS read
+//     V stays row-major and is read with the transposing LDS read
 //     (ds_read_b64_tr_b16): within each 16-lane group, lane s addresses key
 //     row r + s / 4 at dims 4 * (s % 4) .. + 3 of a 16-dim block, and lane d
 //     receives keys r .. r + 3 of dim d of that block (the layout was
 //     measured with a probe on MI355X). Two such reads give a lane its 8
-//     keys; the 288-byte V row stride puts the 4 rows of a read in disjoint
-//     banks.
+//     keys.
 //   * Row statistics move from the score layout (row = lane % 16) to the
 //     output layout (rows 4 * (lane / 16) + j) with ds_bpermute.
 //   * LDS traffic is what bounds the kernel (on MI355X, removing the LDS
-//     operand reads and staging stores made it 44 % faster, removing either
-//     matrix product or the softmax 7-12 %): each tile is staged once into
-//     one 35 KB LDS buffer (loaded into registers one tile ahead, stored
-//     with 16-byte writes, two barriers per tile) and read by all four
-//     wavefronts. With RB = 2 each K
-//     and V operand read serves two row blocks, halving the LDS bytes per
-//     matrix instruction, at two wavefronts per SIMD; RB = 1 keeps three per
-//     SIMD for launches too small to fill the device with 128-row
-//     workgroups (prefill_rows_per_workgroup decides).
+//     operand reads and tile stores made an earlier version 44 % faster,
+//     removing either matrix product or the softmax 7-12 %). With RB = 2
+//     each K and V operand read serves two row blocks, halving the LDS bytes
+//     per matrix instruction; RB = 1 is for launches too small to fill the
+//     device with 128-row workgroups (prefill_rows_per_workgroup decides).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -106,8 +111,6 @@ struct PBF16 {
 
 constexpr int D = kHeadDim;     // 128
 constexpr int kKeys = 64;        // key/value slots per tile
-constexpr int kKStride = D + 8;  // K tile row stride in LDS (u16): 272 B, 4-bank rotation per row
-constexpr int kVStride = D + 16; // V row stride (u16): 288 B, so the 4 rows of a transposing read hit disjoint banks
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ float finite_ref(float m) { return m == kNegInf ? 0.0f : m; }
@@ -141,24 +144,32 @@ __device__ __forceinline__ int visible(int start, int t, int capacity) {
   return n < 0 ? 0 : (n > capacity ? capacity : static_cast<int>(n));
 }
 
+// Slot swizzle of the LDS tiles: row R keeps its 16-byte chunk c in slot
+// c ^ tile_swz(R). Sixteen consecutive rows get sixteen different values (K
+// operand reads of one column by 16 lanes hit all 64 banks once), and four
+// consecutive rows with two adjacent chunks map to eight different slots
+// (the 16 lanes of a transposing V read do too).
+__device__ __forceinline__ int tile_swz(int row) { return 2 * (row % 8) + (row / 8) % 2; }
+
 template <class E, int G, int RB>
-__global__ __launch_bounds__(256, RB == 1 ? 3 : 2) void prefill_kernel(const uint16_t* __restrict__ q,
-                                                      const uint16_t* __restrict__ k_cache,
-                                                      const uint16_t* __restrict__ v_cache,
-                                                      const int32_t* __restrict__ start_arr,
-                                                      uint16_t* __restrict__ out, int n_kv_head, int q_len,
-                                                      int capacity, int units, int row_tiles, float scale_log2) {
-  constexpr int kRows = 64 * RB;  // query rows per workgroup: RB blocks of 16 per wave
-  __shared__ __align__(16) uint16_t s_k[kKeys * kKStride];
-  __shared__ __align__(16) uint16_t s_v[kKeys * kVStride];
+__global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restrict__ q,
+                                                          const uint16_t* __restrict__ k_cache,
+                                                          const uint16_t* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ start_arr,
+                                                          uint16_t* __restrict__ out, int n_kv_head, int q_len,
+                                                          int capacity, int units, int row_tiles, float scale_log2) {
+  constexpr int kRows = 64 * RB;
+  constexpr int kTileU4 = kKeys * D / 8;  // 16-byte chunks per tile (1024)
+  __shared__ __align__(16) uint4 s_k0[kTileU4];
+  __shared__ __align__(16) uint4 s_v0[kTileU4];
+  __shared__ __align__(16) uint4 s_k1[kTileU4];
+  __shared__ __align__(16) uint4 s_v1[kTileU4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int a = lane >> 4;     // 16-lane group
-  const int lr = lane & 15;    // lane within the group
-  // Workgroups of the same (batch row, KV head) are `units` apart; the
-  // longest row tiles (latest tokens, most keys) launch first.
+  const int a = lane >> 4;
+  const int lr = lane & 15;
   const int unit = blockIdx.x % units;
   const int rt = row_tiles - 1 - blockIdx.x / units;
   const int b = unit / n_kv_head;
@@ -175,15 +186,11 @@ __global__ __launch_bounds__(256, RB == 1 ? 3 : 2) void prefill_kernel(const uin
   const uint16_t* kbase = k_cache + head_off;
   const uint16_t* vbase = v_cache + head_off;
 
-  // Row block rb of this wave: rows wave_row0 + 16 rb .. + 15; this lane's
-  // query row in the score layout is row lr of each block.
   const int wave_row0 = r0 + wave * 16 * RB;
   const float cscale = fabsf(scale_log2);
-  // A negative scale is applied as |scale| to the negated query (a sign
-  // flip, exact), so the largest raw score is the largest scaled score.
   const uint32_t sign = scale_log2 < 0.0f ? 0x80008000u : 0u;
   int my_n[RB];
-  uint4 qb[RB][4];  // Q^T operand: dims 32*ks + 8*a .. + 8 of the block's row lr
+  uint4 qb[RB][4];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int my_row = wave_row0 + 16 * rb + lr;
@@ -198,12 +205,10 @@ __global__ __launch_bounds__(256, RB == 1 ? 3 : 2) void prefill_kernel(const uin
       qb[rb][ks] = make_uint4(v.x ^ sign, v.y ^ sign, v.z ^ sign, v.w ^ sign);
     }
   }
-  // Every key of a tile ending at or before this is visible to all of the
-  // wave's rows (rows past the prompt end are never stored).
   const int wave_n_min = wave_row0 < rows ? visible(start, wave_row0 / G, capacity) : 0;
 
   f4 o[RB][8];
-  float m_run[RB], l_run[RB];  // per block: row reference (at most 8 below its max), this lane's weight sum
+  float m_run[RB], l_run[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
@@ -212,38 +217,24 @@ __global__ __launch_bounds__(256, RB == 1 ? 3 : 2) void prefill_kernel(const uin
     l_run[rb] = 0.0f;
   }
 
-  // Tile staging: K and V row-major, 4 row chunks per thread each (16
-  // threads per 256-byte row).
-  uint4 kreg[4], vreg[4];
-  auto load_tile = [&](int tile) {
+  // Wave w loads 1 KB blocks 4w .. 4w + 3 of each tile: block k holds rows
+  // 4k .. 4k + 3, lane l the row 4k + l / 16 chunk (l % 16) ^ swz(row).
+  auto issue_tile = [&](int tile, uint4* sk, uint4* sv) {
     const int base = tile * kKeys;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int idx = tid + 256 * it;
-      const size_t off = static_cast<size_t>(min(base + idx / 16, n_max - 1)) * D + 8 * (idx % 16);
-      kreg[it] = ld16(kbase + off);
-      vreg[it] = ld16(vbase + off);
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int idx = tid + 256 * it;
-      *reinterpret_cast<uint4*>(s_k + (idx / 16) * kKStride + 8 * (idx % 16)) = kreg[it];
-      *reinterpret_cast<uint4*>(s_v + (idx / 16) * kVStride + 8 * (idx % 16)) = vreg[it];
+      const int blk = 4 * wave + it;
+      const int row = 4 * blk + lane / 16;
+      const int chunk = (lane % 16) ^ tile_swz(row);
+      const size_t off = static_cast<size_t>(min(base + row, n_max - 1)) * D + 8 * chunk;
+      __builtin_amdgcn_global_load_lds(kbase + off, sk + 64 * blk, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vbase + off, sv + 64 * blk, 16, 0, 0);
     }
   };
 
-  if (ntiles > 0) load_tile(0);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    __syncthreads();  // every wave is done with the previous tile
-    store_tile();
-    __syncthreads();
-    if (tile + 1 < ntiles) load_tile(tile + 1);
+  auto compute = [&](int tile, const uint4* sk, const uint4* sv) {
+    const uint16_t* sv16 = reinterpret_cast<const uint16_t*>(sv);
     const int base = tile * kKeys;
-
-    // S^T = K Q^T: block nb holds keys base + 16*nb + 4*a + j for the row;
-    // each K operand read serves every row block.
     f4 s[RB][4];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -251,19 +242,18 @@ __global__ __launch_bounds__(256, RB == 1 ? 3 : 2) void prefill_kernel(const uin
       for (int nb = 0; nb < 4; ++nb) s[rb][nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) {
+      const int row = 16 * nb + lr;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint4 kop = *reinterpret_cast<const uint4*>(s_k + (16 * nb + lr) * kKStride + 32 * ks + 8 * a);
+        const uint4 kop = sk[row * 16 + ((4 * ks + a) ^ tile_swz(row))];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) s[rb][nb] = E::mma(kop, qb[rb][ks], s[rb][nb]);
       }
     }
-    const bool full = base + kKeys <= wave_n_min;  // uniform across the wave
+    const bool full = base + kKeys <= wave_n_min;
     uint4 pa[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      // Tile maximum of the raw scores (|scale| >= 0 keeps their order); keys
-      // past a row's own position are masked, on the tiles that reach them.
       bool ok[4][4];
       float mx = kNegInf;
 #pragma unroll
@@ -274,14 +264,12 @@ __global__ __launch_bounds__(256, RB == 1 ? 3 : 2) void prefill_kernel(const uin
           mx = fmaxf(mx, ok[nb][j] ? s[rb][nb][j] : kNegInf);
         }
       }
-      mx = xor32_max(xor16_max(mx));  // over the row's 4 lanes
+      mx = xor32_max(xor16_max(mx));
       const float m_tile = mx == kNegInf ? kNegInf : mx * cscale;
-      // Lazy reference: rescale only when a row's maximum passes its
-      // reference by more than 2^8 (weights stay <= 256).
       const bool grow = m_tile > m_run[rb] + 8.0f;
       if (__builtin_amdgcn_ballot_w64(grow) != 0) {
         const float m_new = grow ? m_tile : m_run[rb];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - finite_ref(m_new));  // 0 while nothing was seen
+        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - finite_ref(m_new));
         m_run[rb] = m_new;
         l_run[rb] *= alpha;
         float al[4];
@@ -294,10 +282,6 @@ __global__ __launch_bounds__(256, RB == 1 ? 3 : 2) void prefill_kernel(const uin
         }
       }
       const float nref = -finite_ref(m_run[rb]);
-      // Weights exp2(|scale| s - m), rounded to the 16-bit type, packed as the
-      // A operand of P V: step ks2 holds keys base + 32*ks2 + 4*a + j (first
-      // half) and base + 32*ks2 + 16 + 4*a + j (second half), j = 0..3. The
-      // row sum adds the rounded weights (a dot with ones, fp32).
 #pragma unroll
       for (int ks2 = 0; ks2 < 2; ++ks2) {
         uint32_t w[4];
@@ -319,19 +303,18 @@ __global__ __launch_bounds__(256, RB == 1 ? 3 : 2) void prefill_kernel(const uin
         pa[rb][ks2] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
-    // O += P V: B operand = V at the same 8 keys, dim 16*db + lr; each V
-    // operand read serves every row block.
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        // Two transposing reads: within each 16-lane group, lane s points at
-        // key row r + s / 4, dims 16*db + 4*(s % 4) .. + 3, and lane d
-        // receives keys r .. r + 3 of dim 16*db + d (r = 32*ks2 + 4*a, then
-        // r + 16): the operand's 8 keys in the order the weights use.
-        const uint16_t* vp = s_v + (32 * ks2 + 4 * a + (lr >> 2)) * kVStride + 16 * db + 4 * (lr & 3);
-        const s4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(vp));
-        const s4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(vp + 16 * kVStride));
+        // rows R and R + 16 (R = 32*ks2 + 4*a + lr / 4), dims 16*db + 4*(lr % 4) .. + 3
+        const int rA = 32 * ks2 + 4 * a + (lr >> 2);
+        const int rB = rA + 16;
+        const int col = 16 * db + 4 * (lr & 3);
+        const uint16_t* pA = sv16 + rA * D + 8 * ((col >> 3) ^ tile_swz(rA)) + (col & 7);
+        const uint16_t* pB = sv16 + rB * D + 8 * ((col >> 3) ^ tile_swz(rB)) + (col & 7);
+        const s4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(pA));
+        const s4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(pB));
         const uint2 w0 = __builtin_bit_cast(uint2, v0);
         const uint2 w1 = __builtin_bit_cast(uint2, v1);
         const uint4 vop = make_uint4(w0.x, w0.y, w1.x, w1.y);
@@ -339,9 +322,21 @@ __global__ __launch_bounds__(256, RB == 1 ? 3 : 2) void prefill_kernel(const uin
         for (int rb = 0; rb < RB; ++rb) o[rb][db] = E::mma(pa[rb][ks2], vop, o[rb][db]);
       }
     }
+  };
+
+  if (ntiles > 0) issue_tile(0, s_k0, s_v0);
+  __syncthreads();  // tile 0 has landed (the barrier waits for the loads)
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    if (tile + 1 < ntiles) issue_tile(tile + 1, s_k1, s_v1);
+    compute(tile, s_k0, s_v0);
+    __syncthreads();  // tile + 1 has landed; every wave is done with buffer 0
+    if (tile + 1 < ntiles) {
+      if (tile + 2 < ntiles) issue_tile(tile + 2, s_k0, s_v0);
+      compute(tile + 1, s_k1, s_v1);
+      __syncthreads();
+    }
   }
 
-  // Normalise and store: lane holds rows 4*a + j of each block, dims 16*db + lr.
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float l_row = xor32_sum(xor16_sum(l_run[rb]));
@@ -418,16 +413,16 @@ hipError_t launch_prefill_e(const PrefillLaunch& p) {
 
 // Two 16-row blocks per wavefront halve the LDS traffic per matrix
 // instruction (each K and V operand read serves both blocks) but halve the
-// workgroup count and allow two waves per SIMD instead of three, so they pay
-// only when the launch still has at least four workgroups per compute unit
-// (measured on MI355X: 15-18 % faster at 4096-8192-token 32/8 prompts, 20 %
-// slower at 1024 tokens, where one workgroup per unit would remain).
+// workgroup count, so they pay only when the launch still has at least two
+// workgroups per compute unit (measured on MI355X: 16 % faster than one
+// block at a 3072-token 32/8 prompt, even at 2048 tokens, slower at 1024,
+// where one workgroup per unit would remain).
 int prefill_rows_per_workgroup(int batch, int n_head, int n_kv_head, int q_len, int num_cus) {
   if (batch <= 0 || n_head <= 0 || n_kv_head <= 0 || q_len <= 0 || num_cus <= 0 || n_head % n_kv_head != 0)
     return 64;
   const long rows = static_cast<long>(n_head / n_kv_head) * q_len;
   const long workgroups = (rows + 127) / 128 * batch * n_kv_head;
-  return workgroups >= 4L * num_cus ? 128 : 64;
+  return workgroups >= 2L * num_cus ? 128 : 64;
 }
 
 hipError_t launch_prefill(const PrefillLaunch& p) {

@@ -326,9 +326,9 @@ int ada_prefill_attn_gqa(const void* q, const void* k_cache, const void* v_cache
  * Query rows per workgroup of ada_prefill_attn_gqa on a device with num_cus
  * compute units: 128 (each wavefront takes two 16-row blocks, so every key
  * and value operand read from LDS serves both) when that still launches at
- * least 4 workgroups per compute unit, i.e.
- *   ceil((n_head / n_kv_head) * q_len / 128) * batch * n_kv_head >= 4 * num_cus,
- * else 64 (one block, three wavefronts per SIMD). 64 for invalid arguments.
+ * least 2 workgroups per compute unit, i.e.
+ *   ceil((n_head / n_kv_head) * q_len / 128) * batch * n_kv_head >= 2 * num_cus,
+ * else 64 (one block per wavefront). 64 for invalid arguments.
  * The choice changes the launch only, not the result beyond rounding order.
  * Pure host arithmetic.
  */

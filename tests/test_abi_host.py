@@ -171,17 +171,18 @@ def test_decode_step_validation(ada):
 
 def test_prefill_rows_per_workgroup_rule(ada):
     """Two 16-row blocks per wavefront (128 rows per workgroup) only when the
-    launch keeps at least 4 workgroups per compute unit."""
+    launch keeps at least 2 workgroups per compute unit."""
     f = ada.prefill_rows_per_workgroup
-    assert f(1, 32, 8, 4096, 256) == 128       # 128 row tiles x 8 units = 1024 = 4 x 256
-    assert f(1, 32, 8, 4095, 256) == 128
-    assert f(1, 32, 8, 4064, 256) == 64        # 127 x 8 = 1016
+    assert f(1, 32, 8, 2048, 256) == 128       # 64 row tiles x 8 units = 512 = 2 x 256
+    assert f(1, 32, 8, 2017, 256) == 128       # 8068 rows: still 64 tiles
+    assert f(1, 32, 8, 2016, 256) == 64        # 8064 rows: 63 x 8 = 504
+    assert f(1, 32, 8, 4096, 256) == 128
     assert f(1, 32, 8, 1024, 256) == 64
     assert f(1, 32, 8, 234, 256) == 64
-    assert f(1, 16, 16, 4096, 256) == 64       # MHA: 32 x 16 = 512
-    assert f(1, 16, 16, 8192, 256) == 128
+    assert f(1, 16, 16, 4096, 256) == 128      # MHA: 32 x 16 = 512
+    assert f(1, 16, 16, 2048, 256) == 64
     assert f(16, 32, 8, 256, 256) == 128       # 8 x 128 units
-    assert f(1, 32, 8, 4096, 512) == 64        # a larger device needs more work
+    assert f(1, 32, 8, 2048, 512) == 64        # a larger device needs more work
     for bad in ((0, 32, 8, 64, 256), (1, 0, 8, 64, 256), (1, 32, 0, 64, 256), (1, 32, 8, 0, 256),
                 (1, 32, 8, 64, 0), (1, 30, 8, 64, 256)):
         assert f(*bad) == 64
