@@ -145,11 +145,18 @@ __device__ __forceinline__ int visible(int start, int t, int capacity) {
 }
 
 // Slot swizzle of the LDS tiles: row R keeps its 16-byte chunk c in slot
-// c ^ tile_swz(R). Sixteen consecutive rows get sixteen different values (K
-// operand reads of one column by 16 lanes hit all 64 banks once), and four
-// consecutive rows with two adjacent chunks map to eight different slots
-// (the 16 lanes of a transposing V read do too).
-__device__ __forceinline__ int tile_swz(int row) { return 2 * (row % 8) + (row / 8) % 2; }
+// c ^ tile_swz(R). The low three bits are a bijection of R mod 8 that sends
+// each aligned group of four rows to values never differing in bit 0 alone,
+// and bit 3 separates the values whose low bits differ only there. Then a
+// 16-byte K operand read of one chunk by 8 or 16 consecutive rows, and a
+// transposing V read (4 rows x 2 adjacent chunks per 16 lanes), touch each
+// bank at most once whether the LDS serves them as 32 or 64 four-byte banks
+// (checked exhaustively on the host).
+__device__ __forceinline__ int tile_swz(int row) {
+  const int x = row & 7;
+  const int sig = ((2 * x) & 7) | (x >> 2);
+  return sig + 8 * ((sig & 1) ^ ((row >> 3) & 1));
+}
 
 template <class E, int G, int RB>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restrict__ q,
