@@ -530,6 +530,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-long-context", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prompt prefill cases and print them (for profiling runs); "
+                         "no contract line")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode kernel needs no exchange between GPUs "
@@ -539,6 +542,9 @@ def main(argv=None):
     import autoregressive_decode_attention_amd as ada
 
     device = torch.device("cuda", 0)
+    if args.prefill_only:
+        print(json.dumps({"prefill": time_prefill(ada, device)}), flush=True)
+        return 0
     torch.cuda.set_device(device)
     # A plain copy of known size (256 MiB read, 256 MiB written): the reference
     # that scales the FETCH_SIZE / WRITE_SIZE counters of the profiled runs.
