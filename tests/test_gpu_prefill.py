@@ -135,6 +135,24 @@ def test_prefill_two_row_blocks(ada, ora, dtype):
         run_prefill(ada, ora, B, Hq, Hkv, T, S, dtype, starts, 880 + k, f"two row blocks {k}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_prefill_full_size_sampled(ada, ora, dtype):
+    """The bench's 4096-token prompt (batch 1, 32/8 heads, capacity 8192, the
+    launch the bench times): token t's outputs are the one-token attention over
+    slots 0..t, so the oracle checks sampled tokens one by one -- the first,
+    tile and row-tile edges, and the last."""
+    B, Hq, Hkv, T, S = 1, 32, 8, 4096, 8192
+    say(f"case prefill full size: B={B} Hq={Hq} Hkv={Hkv} T={T} S={S} {dtype}")
+    q, k, v = prefill_inputs(B, Hq, Hkv, T, S, dtype, [0], 890)
+    scale = 1.0 / math.sqrt(128)
+    out = ada.prefill_attn_gqa(q.cuda(), k.cuda(), v.cuda(), None, scale=scale)
+    torch.cuda.synchronize()
+    got = out.cpu()
+    for t in (0, 1, 15, 16, 31, 32, 63, 64, 127, 1000, 2047, 2048, 3071, 4094, 4095):
+        want = ora.decode(q[:, :, t, :].contiguous(), k, v, [t + 1], scale)
+        assert_parity(got[:, :, t, :], want, dtype, f"token {t}")
+
+
 def test_prefill_rows_match_decode(ada):
     """Token t of the prefill attends what a one-token decode with
     kv_len = start + t + 1 attends: the two kernels agree within the tolerance."""
