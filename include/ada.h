@@ -411,7 +411,9 @@ int ada_decode_combine(const void* workspace, size_t workspace_bytes, int batch,
  * Other arguments as ada_decode_step. Every layer is validated before
  * anything is recorded; an invalid layer returns its ada_decode_step status
  * and creates nothing. Creation records on a private stream of its own and
- * runs no kernel; it is ADA_ERR_HIP if graph capture or instantiation fails.
+ * runs no kernel, so it must not be called while the calling thread is
+ * itself capturing a stream; it is ADA_ERR_HIP if graph capture or
+ * instantiation fails.
  */
 typedef struct ada_step_layer {
   const void* q;
