@@ -476,6 +476,50 @@ def test_decode_step_equals_append_then_decode(ada, ora, dtype):
         assert_parity(fused, want, dtype, f"decode step pos={pos}")
 
 
+@pytest.mark.parametrize("rope", [False, True])
+def test_decode_step_positions_past_the_host_bound(ada, ora, rope):
+    """Device positions beyond max_pos: the row is still written at slot pos[b]
+    (inside the cache) and the row attends over max_pos + 1 slots; negative
+    positions write nothing and give zeros; positions past the cache write
+    nothing. Equal, bit for bit, to the append (or rotary append) followed by
+    the decode with kv_len = min(pos, max_pos) + 1, for per-row, balanced and
+    one-split plans."""
+    B, Hq, Hkv, D, S, dtype = 5, 32, 8, 128, 2048, "bf16"
+    max_pos = 1000
+    pos = [1000, 1500, 2047, -1, 2048]  # at, past the bound (twice), negative, past the cache
+    for k, splits in enumerate((0, 1, 3)):
+        say(f"case decode step past max_pos rope={rope} pos={pos} max_pos={max_pos} splits={splits}")
+        lens = [min(S, max(0, p)) for p in pos]
+        x = W.decode_inputs(W.DecodeShape(B, Hq, Hkv, D, S, dtype), lens, 760 + k, tail="nan")
+        kn, vn = W.append_inputs(B, Hkv, D, dtype, 770 + k)
+        d1, d2 = gpu(x), gpu(x)
+        kn_d, vn_d = kn.cuda(), vn.cuda()
+        pos_t = torch.tensor(pos, dtype=torch.int32, device="cuda")
+        eff = torch.tensor([min(p, max_pos) + 1 if p >= 0 else 0 for p in pos], dtype=torch.int32, device="cuda")
+        if rope:
+            cos, sin = (t.cuda() for t in W.rope_tables([max(0, p) for p in pos], D, dtype))
+            fused = ada.decode_step_rope(d1["q"], kn_d, vn_d, cos, sin, d1["k_cache"], d1["v_cache"], pos_t,
+                                         scale=SCALE, max_pos=max_pos, num_splits=splits)
+            q_rot = ada.rope_kv_append(d2["q"], kn_d, vn_d, cos, sin, d2["k_cache"], d2["v_cache"], pos_t)
+        else:
+            fused = ada.decode_step(d1["q"], kn_d, vn_d, d1["k_cache"], d1["v_cache"], pos_t, scale=SCALE,
+                                    max_pos=max_pos, num_splits=splits)
+            ada.kv_append(kn_d, vn_d, d2["k_cache"], d2["v_cache"], pos_t)
+            q_rot = d2["q"]
+        ref = ada.decode_attn_gqa_ex(q_rot, d2["k_cache"], d2["v_cache"], eff, scale=SCALE,
+                                     max_kv_len=max_pos + 1, num_splits=splits)
+        torch.cuda.synchronize()
+        assert torch.equal(d1["k_cache"].view(torch.int16), d2["k_cache"].view(torch.int16)), "key rows differ"
+        assert torch.equal(d1["v_cache"].view(torch.int16), d2["v_cache"].view(torch.int16)), "value rows differ"
+        assert torch.equal(fused, ref), "decode step differs from append + decode"
+        assert torch.count_nonzero(fused[3]) == 0, "a negative position must give a zero row"
+        if not rope:
+            kc, vc = ora.kv_append(kn, vn, x["k_cache"], x["v_cache"], pos)
+            to16 = lambda a: torch.from_numpy(a.view(np.int16)).view(W.TORCH_DTYPES[dtype])
+            want = ora.decode(x["q"], to16(kc), to16(vc), eff.tolist(), SCALE)
+            assert_parity(fused, want, dtype, f"decode step past max_pos splits={splits}")
+
+
 def test_decode_step_position_zero_returns_new_value(ada):
     """Position 0: the only slot is the new one, so out = v_new exactly."""
     x = gpu(W.decode_inputs(shape(2, 16, 4, 64, "bf16"), [0, 0], 760, tail="nan"))
