@@ -64,6 +64,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ada_internal.h"
 
 namespace ada {
@@ -239,7 +241,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
     }
   };
 
-  auto compute = [&](int tile, const uint4* sk, const uint4* sv) {
+  // FULL: every key of the tile is visible to every row of the wavefront
+  // (no causal mask on this tile).
+  auto compute = [&](int tile, const uint4* sk, const uint4* sv, auto full_tile) __attribute__((always_inline)) {
+    constexpr bool full = decltype(full_tile)::value;
     const uint16_t* sv16 = reinterpret_cast<const uint16_t*>(sv);
     const int base = tile * kKeys;
     f4 s[RB][4];
@@ -257,7 +262,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
         for (int rb = 0; rb < RB; ++rb) s[rb][nb] = E::mma(kop, qb[rb][ks], s[rb][nb]);
       }
     }
-    const bool full = base + kKeys <= wave_n_min;
     uint4 pa[RB][2];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -299,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
           for (int jj = 0; jj < 2; ++jj) {
             float p0 = __builtin_amdgcn_exp2f(fmaf(s[rb][nb][2 * jj], cscale, nref));
             float p1 = __builtin_amdgcn_exp2f(fmaf(s[rb][nb][2 * jj + 1], cscale, nref));
-            if (!full) {
+            if constexpr (!full) {
               p0 = ok[nb][2 * jj] ? p0 : 0.0f;
               p1 = ok[nb][2 * jj + 1] ? p1 : 0.0f;
             }
@@ -331,15 +335,28 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
     }
   };
 
+  // Tiles wholly below the wavefront's smallest causal limit take the
+  // unmasked body. Every lane of a wavefront takes the same side, so the
+  // other side is skipped. (With the wave index in a scalar register the
+  // test would be a scalar branch, but the register allocator then spills
+  // the two-block kernel.)
+  auto compute_tile = [&](int tile, const uint4* sk, const uint4* sv) __attribute__((always_inline)) {
+    if ((tile + 1) * kKeys <= wave_n_min) {
+      compute(tile, sk, sv, std::true_type{});
+    } else {
+      compute(tile, sk, sv, std::false_type{});
+    }
+  };
+
   if (ntiles > 0) issue_tile(0, s_k0, s_v0);
   __syncthreads();  // tile 0 has landed (the barrier waits for the loads)
   for (int tile = 0; tile < ntiles; tile += 2) {
     if (tile + 1 < ntiles) issue_tile(tile + 1, s_k1, s_v1);
-    compute(tile, s_k0, s_v0);
+    compute_tile(tile, s_k0, s_v0);
     __syncthreads();  // tile + 1 has landed; every wave is done with buffer 0
     if (tile + 1 < ntiles) {
       if (tile + 2 < ntiles) issue_tile(tile + 2, s_k0, s_v0);
-      compute(tile + 1, s_k1, s_v1);
+      compute_tile(tile + 1, s_k1, s_v1);
       __syncthreads();
     }
   }
