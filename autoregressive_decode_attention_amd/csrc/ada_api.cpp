@@ -434,6 +434,8 @@ int ada_prefill_attn_gqa(const void* q, const void* k_cache, const void* v_cache
   if (n_head % n_kv_head != 0 || n_head / n_kv_head > ada::kMaxGroup) return ADA_ERR_GQA;
   if (head_dim != ada::kHeadDim) return ADA_ERR_HEAD_DIM;
   if (!std::isfinite(scale)) return ADA_ERR_SCALE;
+  // the kernel addresses one KV head's slab with 32-bit byte offsets
+  if (static_cast<int64_t>(capacity) * head_dim * 2 > INT32_MAX) return ADA_ERR_SHAPE;
   const int64_t row_tiles = ceil_div(static_cast<int64_t>(n_head / n_kv_head) * q_len, 64);
   if (row_tiles * batch * n_kv_head > INT32_MAX) return ADA_ERR_SHAPE;
   if (static_cast<int64_t>(batch) * n_head * q_len * head_dim > (int64_t(1) << 40)) return ADA_ERR_SHAPE;

@@ -228,16 +228,27 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
 
   // Wave w loads 1 KB blocks 4w .. 4w + 3 of each tile: block k holds rows
   // 4k .. 4k + 3, lane l the row 4k + l / 16 chunk (l % 16) ^ swz(row).
+  // Buffer loads over the (batch row, KV head) slab take 32-bit byte offsets
+  // (the host keeps capacity * 256 bytes below 2^31), so a row costs three
+  // integer instructions instead of 64-bit address arithmetic; the LDS
+  // destination is wave-uniform (scalar).
+  const __amdgpu_buffer_rsrc_t k_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kbase), static_cast<short>(0), 0x7fffffff, 0x00020000);
+  const __amdgpu_buffer_rsrc_t v_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vbase), static_cast<short>(0), 0x7fffffff, 0x00020000);
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   auto issue_tile = [&](int tile, uint4* sk, uint4* sv) {
     const int base = tile * kKeys;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int blk = 4 * wave + it;
-      const int row = 4 * blk + lane / 16;
+      const int row = 16 * wave + 4 * it + lane / 16;
       const int chunk = (lane % 16) ^ tile_swz(row);
-      const size_t off = static_cast<size_t>(min(base + row, n_max - 1)) * D + 8 * chunk;
-      __builtin_amdgcn_global_load_lds(kbase + off, sk + 64 * blk, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vbase + off, sv + 64 * blk, 16, 0, 0);
+      const uint32_t off = (static_cast<uint32_t>(min(base + row, n_max - 1)) << 8) | (chunk << 4);
+      const int blk = 4 * wave_s + it;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(k_rsrc, (__attribute__((address_space(3))) void*)(sk + 64 * blk), 16,
+                                               off, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(v_rsrc, (__attribute__((address_space(3))) void*)(sv + 64 * blk), 16,
+                                               off, 0, 0, 0);
     }
   };
 

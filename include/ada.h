@@ -315,8 +315,10 @@ int ada_prefill_append(const void* k_new, const void* v_new, void* k_cache, void
  *   start      device int32 [batch], or NULL: every row starts at slot 0.
  *   scale      finite float (1/sqrt(head_dim) is SDPA's default).
  * n_head a multiple of n_kv_head with n_head / n_kv_head in 1..8 (ADA_ERR_GQA);
- * head_dim 128; buffers 16-byte aligned; ADA_OK without work for batch == 0
- * or q_len == 0. One kernel launch on `stream`, no workspace.
+ * head_dim 128; capacity below 2^23 slots (one KV head's slab under 2 GiB,
+ * addressed with 32-bit offsets; else ADA_ERR_SHAPE); buffers 16-byte
+ * aligned; ADA_OK without work for batch == 0 or q_len == 0. One kernel
+ * launch on `stream`, no workspace.
  */
 int ada_prefill_attn_gqa(const void* q, const void* k_cache, const void* v_cache, const int32_t* start, int batch,
                          int n_head, int n_kv_head, int q_len, int head_dim, int capacity, float scale, int dtype,

@@ -265,7 +265,8 @@ def test_prefill_validation(ada):
     f = ada._lib.ada_prefill_attn_gqa
     # q, k, v, start, B, Hq, Hkv, T, D, S, scale, dtype, out, stream
     args = lambda **kw: [kw.get("q", P), kw.get("k", P2), kw.get("v", P3), NUL, kw.get("B", 1), kw.get("Hq", 32),
-                         kw.get("Hkv", 8), kw.get("T", 16), kw.get("D", 128), 64, ctypes.c_float(kw.get("scale", 0.08)),
+                         kw.get("Hkv", 8), kw.get("T", 16), kw.get("D", 128), kw.get("S", 64),
+                         ctypes.c_float(kw.get("scale", 0.08)),
                          kw.get("dtype", 0), kw.get("out", P4), NUL]
     assert f(*args(dtype=2)) == -4
     assert f(*args(Hq=12)) == -3
@@ -277,6 +278,8 @@ def test_prefill_validation(ada):
     assert f(*args(out=NUL)) == -1
     assert f(*args(q=MIS)) == -9
     assert f(*args(T=0, q=NUL, k=NUL, v=NUL, out=NUL)) == 0
+    assert f(*args(S=1 << 23)) == -2          # a KV head's slab must stay under 2 GiB (32-bit offsets)
+    assert f(*args(S=1 << 23, T=0)) == -2
     g = ada._lib.ada_prefill_append
     gargs = lambda **kw: [kw.get("kn", P), P2, P3, P4, NUL, kw.get("B", 1), 8, kw.get("T", 16), 64, kw.get("D", 128),
                           kw.get("dtype", 1), NUL]
