@@ -160,6 +160,139 @@ __device__ __forceinline__ int tile_swz(int row) {
   return sig + 8 * ((sig & 1) ^ ((row >> 3) & 1));
 }
 
+// Scores of one 64-key tile for RB blocks of 16 query rows, S^T = K Q^T:
+// s[rb][nb] holds, for the lane's query row (lane % 16 of block rb), keys
+// 16 * nb + 4 * (lane / 16) .. + 3 of the tile. Each K operand read from LDS
+// serves all RB blocks.
+template <class E, int RB>
+__device__ __forceinline__ void tile_scores(const uint4* sk, const uint4 (&qb)[RB][4], int lr, int a, f4 (&s)[RB][4]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) s[rb][nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int row = 16 * nb + lr;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 kop = sk[row * 16 + ((4 * ks + a) ^ tile_swz(row))];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) s[rb][nb] = E::mma(kop, qb[rb][ks], s[rb][nb]);
+    }
+  }
+}
+
+// Online softmax of one tile's scores (keys base .. base + 63). FULL: every
+// key is within every row's causal limit, so nothing is masked. Moves the
+// running reference m_run (rescaling o and l_run) when a row's maximum
+// passes it by more than 2^8, adds the tile's weights to l_run and leaves
+// them, rounded to 16 bits, in pa as the A operand of the P V product.
+template <class E, int RB, bool FULL>
+__device__ __forceinline__ void tile_softmax(const f4 (&s)[RB][4], int base, const int (&my_n)[RB], int a,
+                                             float cscale, float (&m_run)[RB], float (&l_run)[RB], f4 (&o)[RB][8],
+                                             uint4 (&pa)[RB][2]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    bool ok[4][4];
+    float mx = kNegInf;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ok[nb][j] = FULL || base + 16 * nb + 4 * a + j < my_n[rb];
+        mx = fmaxf(mx, ok[nb][j] ? s[rb][nb][j] : kNegInf);
+      }
+    }
+    mx = xor32_max(xor16_max(mx));
+    const float m_tile = mx == kNegInf ? kNegInf : mx * cscale;
+    const bool grow = m_tile > m_run[rb] + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? m_tile : m_run[rb];
+      const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - finite_ref(m_new));
+      m_run[rb] = m_new;
+      l_run[rb] *= alpha;
+      float al[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) al[j] = from_lane(alpha, 4 * a + j);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[rb][db][j] *= al[j];
+      }
+    }
+    const float nref = -finite_ref(m_run[rb]);
+#pragma unroll
+    for (int ks2 = 0; ks2 < 2; ++ks2) {
+      uint32_t w[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int nb = 2 * ks2 + h;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          float p0 = __builtin_amdgcn_exp2f(fmaf(s[rb][nb][2 * jj], cscale, nref));
+          float p1 = __builtin_amdgcn_exp2f(fmaf(s[rb][nb][2 * jj + 1], cscale, nref));
+          if constexpr (!FULL) {
+            p0 = ok[nb][2 * jj] ? p0 : 0.0f;
+            p1 = ok[nb][2 * jj + 1] ? p1 : 0.0f;
+          }
+          w[2 * h + jj] = E::pack(p0, p1);
+          l_run[rb] = E::sum2(w[2 * h + jj], l_run[rb]);
+        }
+      }
+      pa[rb][ks2] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+// O += P V over one tile for RB row blocks. V stays row-major in LDS and is
+// read with the transposing LDS read; each V operand serves all RB blocks.
+template <class E, int RB>
+__device__ __forceinline__ void tile_pv(const uint4* sv, const uint4 (&pa)[RB][2], int lr, int a, f4 (&o)[RB][8]) {
+  const uint16_t* sv16 = reinterpret_cast<const uint16_t*>(sv);
+#pragma unroll
+  for (int ks2 = 0; ks2 < 2; ++ks2) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      // rows R and R + 16 (R = 32*ks2 + 4*a + lr / 4), dims 16*db + 4*(lr % 4) .. + 3
+      const int rA = 32 * ks2 + 4 * a + (lr >> 2);
+      const int rB = rA + 16;
+      const int col = 16 * db + 4 * (lr & 3);
+      const uint16_t* pA = sv16 + rA * D + 8 * ((col >> 3) ^ tile_swz(rA)) + (col & 7);
+      const uint16_t* pB = sv16 + rB * D + 8 * ((col >> 3) ^ tile_swz(rB)) + (col & 7);
+      const s4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(pA));
+      const s4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(pB));
+      const uint2 w0 = __builtin_bit_cast(uint2, v0);
+      const uint2 w1 = __builtin_bit_cast(uint2, v1);
+      const uint4 vop = make_uint4(w0.x, w0.y, w1.x, w1.y);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o[rb][db] = E::mma(pa[rb][ks2], vop, o[rb][db]);
+    }
+  }
+}
+
+// Normalised rows of o to the output ([B, H_q, T, D], rounded to nearest
+// even); rows past the head group's last are skipped.
+template <class E, int G, int RB>
+__device__ __forceinline__ void store_rows(const f4 (&o)[RB][8], const float (&l_run)[RB], uint16_t* out, int wave_row0,
+                                           int rows, int b, int g, int n_head, int q_len, int lr, int a) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l_row = xor32_sum(xor16_sum(l_run[rb]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lj = from_lane(l_row, 4 * a + j);
+      const int row = wave_row0 + 16 * rb + 4 * a + j;
+      if (row >= rows) continue;
+      const int t = row / G;
+      const int i = row % G;
+      uint16_t* orow = out + ((static_cast<size_t>(b) * n_head + g * G + i) * q_len + t) * D;
+      const float inv = lj > 0.0f ? 1.0f / lj : 0.0f;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) orow[16 * db + lr] = static_cast<uint16_t>(E::round(o[rb][db][j] * inv));
+    }
+  }
+}
+
 template <class E, int G, int RB>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k_cache,
@@ -252,98 +385,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
     }
   };
 
-  // FULL: every key of the tile is visible to every row of the wavefront
-  // (no causal mask on this tile).
+  // full_tile: every key of the tile is visible to every row of the
+  // wavefront (no causal mask on this tile).
   auto compute = [&](int tile, const uint4* sk, const uint4* sv, auto full_tile) __attribute__((always_inline)) {
-    constexpr bool full = decltype(full_tile)::value;
-    const uint16_t* sv16 = reinterpret_cast<const uint16_t*>(sv);
-    const int base = tile * kKeys;
     f4 s[RB][4];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) s[rb][nb] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int row = 16 * nb + lr;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const uint4 kop = sk[row * 16 + ((4 * ks + a) ^ tile_swz(row))];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s[rb][nb] = E::mma(kop, qb[rb][ks], s[rb][nb]);
-      }
-    }
     uint4 pa[RB][2];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      bool ok[4][4];
-      float mx = kNegInf;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          ok[nb][j] = full || base + 16 * nb + 4 * a + j < my_n[rb];
-          mx = fmaxf(mx, ok[nb][j] ? s[rb][nb][j] : kNegInf);
-        }
-      }
-      mx = xor32_max(xor16_max(mx));
-      const float m_tile = mx == kNegInf ? kNegInf : mx * cscale;
-      const bool grow = m_tile > m_run[rb] + 8.0f;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = grow ? m_tile : m_run[rb];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[rb] - finite_ref(m_new));
-        m_run[rb] = m_new;
-        l_run[rb] *= alpha;
-        float al[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) al[j] = from_lane(alpha, 4 * a + j);
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[rb][db][j] *= al[j];
-        }
-      }
-      const float nref = -finite_ref(m_run[rb]);
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        uint32_t w[4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int nb = 2 * ks2 + h;
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            float p0 = __builtin_amdgcn_exp2f(fmaf(s[rb][nb][2 * jj], cscale, nref));
-            float p1 = __builtin_amdgcn_exp2f(fmaf(s[rb][nb][2 * jj + 1], cscale, nref));
-            if constexpr (!full) {
-              p0 = ok[nb][2 * jj] ? p0 : 0.0f;
-              p1 = ok[nb][2 * jj + 1] ? p1 : 0.0f;
-            }
-            w[2 * h + jj] = E::pack(p0, p1);
-            l_run[rb] = E::sum2(w[2 * h + jj], l_run[rb]);
-          }
-        }
-        pa[rb][ks2] = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-    }
-#pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        // rows R and R + 16 (R = 32*ks2 + 4*a + lr / 4), dims 16*db + 4*(lr % 4) .. + 3
-        const int rA = 32 * ks2 + 4 * a + (lr >> 2);
-        const int rB = rA + 16;
-        const int col = 16 * db + 4 * (lr & 3);
-        const uint16_t* pA = sv16 + rA * D + 8 * ((col >> 3) ^ tile_swz(rA)) + (col & 7);
-        const uint16_t* pB = sv16 + rB * D + 8 * ((col >> 3) ^ tile_swz(rB)) + (col & 7);
-        const s4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(pA));
-        const s4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4*)(pB));
-        const uint2 w0 = __builtin_bit_cast(uint2, v0);
-        const uint2 w1 = __builtin_bit_cast(uint2, v1);
-        const uint4 vop = make_uint4(w0.x, w0.y, w1.x, w1.y);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) o[rb][db] = E::mma(pa[rb][ks2], vop, o[rb][db]);
-      }
-    }
+    tile_scores<E, RB>(sk, qb, lr, a, s);
+    tile_softmax<E, RB, decltype(full_tile)::value>(s, tile * kKeys, my_n, a, cscale, m_run, l_run, o, pa);
+    tile_pv<E, RB>(sv, pa, lr, a, o);
   };
 
   // Tiles wholly below the wavefront's smallest causal limit take the
@@ -372,22 +421,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
     }
   }
 
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float l_row = xor32_sum(xor16_sum(l_run[rb]));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float lj = from_lane(l_row, 4 * a + j);
-      const int row = wave_row0 + 16 * rb + 4 * a + j;
-      if (row >= rows) continue;
-      const int t = row / G;
-      const int i = row % G;
-      uint16_t* orow = out + ((static_cast<size_t>(b) * n_head + g * G + i) * q_len + t) * D;
-      const float inv = lj > 0.0f ? 1.0f / lj : 0.0f;
-#pragma unroll
-      for (int db = 0; db < 8; ++db) orow[16 * db + lr] = static_cast<uint16_t>(E::round(o[rb][db][j] * inv));
-    }
-  }
+  store_rows<E, G, RB>(o, l_run, out, wave_row0, rows, b, g, n_head, q_len, lr, a);
 }
 
 // Prompt append: row t of every (batch row, KV head) to slot start[b] + t,
