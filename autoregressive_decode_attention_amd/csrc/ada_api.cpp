@@ -245,11 +245,16 @@ int prepare_decode(const void* q, const void* k_cache, const void* v_cache, cons
 // balanced plan (each workgroup reads every row's length to find its range).
 constexpr int kBalancedMaxBatch = 64;
 
+// Prefixes up to which the balanced plan is used: the kernels sum the rows'
+// lengths in 32 bits (64 rows of at most 2^25 slots).
+constexpr int kBalancedMaxLen = 1 << 25;
+
 // Use the balanced split plan? Only for heuristic split counts (a forced
 // count keeps the per-row ranges it asks for), lengths that only the device
 // knows, more than one row and at least two splits per row.
 bool use_balanced(const ada::DecodeLaunch& p, bool device_lengths, int num_splits) {
-  return device_lengths && num_splits == 0 && p.batch >= 2 && p.batch <= kBalancedMaxBatch && p.splits >= 2;
+  return device_lengths && num_splits == 0 && p.batch >= 2 && p.batch <= kBalancedMaxBatch && p.splits >= 2 &&
+         p.max_kv_len <= kBalancedMaxLen;
 }
 
 int check_workspace(const void* workspace, size_t workspace_bytes, int batch, int n_head,

@@ -278,6 +278,29 @@ __device__ __forceinline__ int row_length(const int32_t* kv_len, const int32_t* 
   return n < 0 ? 0 : (n > max_kv_len ? max_kv_len : n);
 }
 
+// Integer sum over the 64 lanes of a wavefront (every lane gets it); all
+// lanes must be active.
+__device__ __forceinline__ unsigned wave_sum_u32(unsigned x) {
+  x += static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kDppXor1, 0xF, 0xF, false));
+  x += static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kDppXor2, 0xF, 0xF, false));
+  x += static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kDppHalfMirror, 0xF, 0xF, false));
+  x += static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kDppRor8, 0xF, 0xF, false));
+  auto r16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = r16[0] + r16[1];
+  auto r32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return r32[0] + r32[1];
+}
+
+// Inclusive prefix sum over the lanes of a wavefront; all lanes active.
+__device__ __forceinline__ unsigned wave_inclusive_scan(unsigned x, int lane) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const unsigned y = static_cast<unsigned>(__shfl_up(static_cast<int>(x), d, 64));
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
 // Balanced split plan for batches whose lengths live on the device (so the
 // host cannot size the splits per row): the `slots` workgroups of a KV head
 // are shared by all rows with one common chunk c (a multiple of the 64-slot
@@ -286,21 +309,40 @@ __device__ __forceinline__ int row_length(const int32_t* kv_len, const int32_t* 
 // times), else ceil(total / (slots - batch)) rounded up, which always fits
 // (each row wastes less than one chunk). Every kernel of a call derives the
 // same plan from the same lengths.
-__device__ __forceinline__ int balanced_chunk(const int32_t* kv_len, const int32_t* pos, bool step, int max_kv_len,
-                                              int batch, int slots) {
-  long total = 0;
-  for (int b = 0; b < batch; ++b) total += row_length(kv_len, pos, step, max_kv_len, b);
-  long c = (total + slots - 1) / slots;
-  c = c < kTileRows ? kTileRows : (c + kTileRows - 1) / kTileRows * kTileRows;
-  for (int tries = 0; tries < 8; ++tries, c += kTileRows) {
-    long used = 0;
-    for (int b = 0; b < batch; ++b) used += (row_length(kv_len, pos, step, max_kv_len, b) + c - 1) / c;
-    if (used <= slots) return static_cast<int>(c);
+//
+// Evaluated by a whole wavefront, one batch row per lane (batch <= 64, all
+// lanes active): lane-parallel divisions and cross-lane sums instead of a
+// serial walk over the rows. The host keeps max_kv_len <= 2^25 on this path,
+// so every sum fits in 32 bits. Returns, for the lane's row (zeros for lanes
+// past the batch), its first slot and slot count; the chunk is the same in
+// every lane.
+struct BalancedRows {
+  int chunk;
+  int first;  // first workgroup slot of this lane's row
+  int count;  // slots of this lane's row
+};
+
+__device__ __forceinline__ BalancedRows balanced_rows(const int32_t* kv_len, const int32_t* pos, bool step,
+                                                      int max_kv_len, int batch, int slots, int lane) {
+  const unsigned n = lane < batch ? static_cast<unsigned>(row_length(kv_len, pos, step, max_kv_len, lane)) : 0u;
+  const unsigned total = wave_sum_u32(n);
+  const unsigned tile = kTileRows;
+  auto round_tile = [&](unsigned c) { return c < tile ? tile : (c + tile - 1) / tile * tile; };
+  unsigned c = round_tile((total + slots - 1) / slots);
+  bool fits = false;
+  for (int tries = 0; tries < 8; ++tries, c += tile) {
+    if (wave_sum_u32((n + c - 1) / c) <= static_cast<unsigned>(slots)) {
+      fits = true;
+      break;
+    }
   }
-  const long free = slots - batch;  // >= batch: the host asks for >= 2 slots per row
-  long safe = (total + free - 1) / free;
-  safe = safe < kTileRows ? kTileRows : (safe + kTileRows - 1) / kTileRows * kTileRows;
-  return static_cast<int>(safe);
+  if (!fits) {
+    const unsigned free = slots - batch;  // >= batch: the host asks for >= 2 slots per row
+    c = round_tile((total + free - 1) / free);
+  }
+  const unsigned count = (n + c - 1) / c;
+  const unsigned incl = wave_inclusive_scan(count, lane);
+  return {static_cast<int>(c), static_cast<int>(incl - count), static_cast<int>(count)};
 }
 
 struct SplitRange {
@@ -333,21 +375,18 @@ __device__ __forceinline__ bool begin_split(SplitRange& r, uint16_t* k_cache, ui
   int b = blockIdx.z;
   size_t slot = static_cast<size_t>(split) * gridDim.z + b;  // partial slot (split-major)
   if (chunk == 0) {
-    // Balanced plan: this workgroup is slot z * splits + x of its KV head.
+    // Balanced plan: this workgroup is slot z * splits + x of its KV head;
+    // its row is the one whose slot range holds it.
     const int idx = blockIdx.z * gridDim.x + blockIdx.x;
-    chunk = balanced_chunk(kv_len, pos, k_new != nullptr, max_kv_len, gridDim.z, gridDim.x * gridDim.z);
-    int first = 0;
-    b = -1;
-    for (int bb = 0; bb < static_cast<int>(gridDim.z); ++bb) {
-      const int sb = (row_length(kv_len, pos, k_new != nullptr, max_kv_len, bb) + chunk - 1) / chunk;
-      if (idx < first + sb) {
-        b = bb;
-        split = idx - first;
-        break;
-      }
-      first += sb;
-    }
-    if (b < 0) return false;  // a slot no row needs: nothing to write
+    const int lane = tid & 63;
+    const BalancedRows rows = balanced_rows(kv_len, pos, k_new != nullptr, max_kv_len, gridDim.z,
+                                            gridDim.x * gridDim.z, lane);
+    chunk = rows.chunk;
+    const unsigned long long hit =
+        __ballot(lane < static_cast<int>(gridDim.z) && idx >= rows.first && idx < rows.first + rows.count);
+    if (hit == 0) return false;  // a slot no row needs: nothing to write
+    b = __ffsll(hit) - 1;
+    split = idx - __shfl(rows.first, b, 64);
     slot = idx;
   }
   r.head_off = (static_cast<size_t>(b) * n_kv_head + g) * static_cast<size_t>(capacity) * D;
@@ -754,10 +793,9 @@ __global__ __launch_bounds__(64 * kMaxGroup) void combine_kernel(
   uint32_t split_stride = static_cast<uint32_t>(gridDim.y) * n_head;
   if (balanced) {
     const int slots = num_splits * static_cast<int>(gridDim.y);
-    const int chunk = balanced_chunk(kv_len, pos, step != 0, max_kv_len, gridDim.y, slots);
-    int first = 0;
-    for (int bb = 0; bb < b; ++bb) first += (row_length(kv_len, pos, step != 0, max_kv_len, bb) + chunk - 1) / chunk;
-    num_splits = (row_length(kv_len, pos, step != 0, max_kv_len, b) + chunk - 1) / chunk;
+    const BalancedRows rows = balanced_rows(kv_len, pos, step != 0, max_kv_len, gridDim.y, slots, lane);
+    const int first = __shfl(rows.first, b, 64);
+    num_splits = __shfl(rows.count, b, 64);
     row0 = static_cast<uint32_t>(first) * n_head + static_cast<uint32_t>(g) * group + i;
     split_stride = n_head;
   }
