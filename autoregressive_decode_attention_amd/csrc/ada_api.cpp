@@ -10,6 +10,7 @@
 #include <cmath>
 #include <climits>
 #include <cstdint>
+#include <initializer_list>
 #include <vector>
 
 #include "ada_internal.h"
@@ -28,6 +29,17 @@ int hip_fail(hipError_t e) {
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Product of non-negative factors, saturated at INT64_MAX: size checks on
+// arguments of any magnitude never overflow.
+int64_t sat_mul(std::initializer_list<int64_t> factors) {
+  __int128 p = 1;
+  for (int64_t f : factors) {
+    p *= f;
+    if (p > INT64_MAX) return INT64_MAX;
+  }
+  return static_cast<int64_t>(p);
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -152,6 +164,8 @@ int ada_decode_num_splits(int batch, int n_head, int n_kv_head, int max_kv_len, 
 
 size_t ada_decode_workspace_bytes(int batch, int n_head, int n_kv_head, int head_dim, int num_splits) {
   if (num_splits < 1 || batch <= 0 || n_head <= 0 || n_kv_head <= 0 || head_dim <= 0) return 0;
+  // sizes no call could use (and that would wrap size_t) report 0
+  if (sat_mul({batch, n_head, num_splits, static_cast<int64_t>(head_dim) + 2, 4}) > (int64_t(1) << 56)) return 0;
   return ada::workspace_layout(batch, n_head, n_kv_head, head_dim, num_splits).total;
 }
 
@@ -178,8 +192,8 @@ int ada_rope_kv_append(const void* q, void* q_out, const void* k_new, const void
   if (head_dim != ada::kHeadDim) return ADA_ERR_HEAD_DIM;
   if ((q == nullptr) != (q_out == nullptr)) return ADA_ERR_NULL;
   if (q != nullptr && n_head <= 0) return ADA_ERR_SHAPE;
-  const int64_t rows = static_cast<int64_t>(batch) * ((q ? n_head : 0) + n_kv_head);
-  if (rows * 16 > INT32_MAX - 255) return ADA_ERR_SHAPE;
+  const int64_t heads = (q ? static_cast<int64_t>(n_head) : 0) + n_kv_head;
+  if (sat_mul({batch, heads, 16}) > INT32_MAX - 255) return ADA_ERR_SHAPE;
   if (batch == 0) return ADA_OK;
   if (!k_new || !v_new || !cos || !sin || !k_cache || !v_cache || !pos) return ADA_ERR_NULL;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(cos) || !aligned16(sin) ||
@@ -421,7 +435,7 @@ int ada_prefill_append(const void* k_new, const void* v_new, void* k_cache, void
   if (dtype != ADA_F16 && dtype != ADA_BF16) return ADA_ERR_DTYPE;
   if (batch < 0 || n_kv_head <= 0 || q_len < 0 || capacity <= 0) return ADA_ERR_SHAPE;
   if (head_dim != ada::kHeadDim) return ADA_ERR_HEAD_DIM;
-  const int64_t chunks = static_cast<int64_t>(batch) * n_kv_head * q_len * (ada::kHeadDim * 2 / 16);
+  const int64_t chunks = sat_mul({batch, n_kv_head, q_len, ada::kHeadDim * 2 / 16});
   if ((chunks + 255) / 256 > INT32_MAX) return ADA_ERR_SHAPE;
   if (batch == 0 || q_len == 0) return ADA_OK;
   if (!k_new || !v_new || !k_cache || !v_cache) return ADA_ERR_NULL;  // start may be NULL (slot 0)
@@ -441,9 +455,9 @@ int ada_prefill_attn_gqa(const void* q, const void* k_cache, const void* v_cache
   if (!std::isfinite(scale)) return ADA_ERR_SCALE;
   // the kernel addresses one KV head's slab with 32-bit byte offsets
   if (static_cast<int64_t>(capacity) * head_dim * 2 > INT32_MAX) return ADA_ERR_SHAPE;
-  const int64_t row_tiles = ceil_div(static_cast<int64_t>(n_head / n_kv_head) * q_len, 64);
-  if (row_tiles * batch * n_kv_head > INT32_MAX) return ADA_ERR_SHAPE;
-  if (static_cast<int64_t>(batch) * n_head * q_len * head_dim > (int64_t(1) << 40)) return ADA_ERR_SHAPE;
+  const int64_t row_tiles = ceil_div(sat_mul({n_head / n_kv_head, q_len}), 64);
+  if (sat_mul({row_tiles, batch, n_kv_head}) > INT32_MAX) return ADA_ERR_SHAPE;
+  if (sat_mul({batch, n_head, q_len, head_dim}) > (int64_t(1) << 40)) return ADA_ERR_SHAPE;
   if (batch == 0 || q_len == 0) return ADA_OK;
   if (!q || !k_cache || !v_cache || !out) return ADA_ERR_NULL;  // start may be NULL (slot 0)
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out)) return ADA_ERR_ALIGN;

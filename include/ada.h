@@ -156,7 +156,8 @@ int ada_decode_num_splits(int batch, int n_head, int n_kv_head, int max_kv_len, 
  * results: a running maximum and sum (2 floats) and an unnormalised
  * accumulator (head_dim floats) per (split, batch row, query head), stored
  * split-major, each array rounded up to 256 bytes. Returns 0 for
- * num_splits < 1 or non-positive sizes. ada_decode_attn_gqa needs this much
+ * num_splits < 1, non-positive sizes, or a size beyond 2^56 bytes (no call
+ * can use it). ada_decode_attn_gqa needs this much
  * only when it uses 2 or more splits. n_kv_head is accepted for symmetry
  * with the decode calls. Pure host arithmetic.
  */

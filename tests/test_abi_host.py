@@ -300,6 +300,10 @@ def test_workspace_bytes_arithmetic(ada):
     assert ada.decode_workspace_bytes(8, 32, 8, 128, 1) == r256(8 * 32 * 8) + r256(8 * 32 * 512)
     assert ada.decode_workspace_bytes(8, 32, 8, 128, 0) == 0
     assert ada.decode_workspace_bytes(0, 32, 8, 128, 4) == 0
+    # sizes no call can use report 0 instead of wrapping
+    assert ada.decode_workspace_bytes(2**31 - 1, 2**31 - 1, 1, 128, 256) == 0
+    assert ada.decode_workspace_bytes(65535, 8 * 65535, 65535, 128, 256) == r256(65535 * 8 * 65535 * 256 * 8) + \
+        r256(65535 * 8 * 65535 * 256 * 512)
 
 
 def test_split_heuristic_properties(ada):
