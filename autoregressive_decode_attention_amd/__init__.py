@@ -12,12 +12,17 @@ The functions keep the C names without the ``ada_`` prefix:
 * ``decode_attn_gqa(q, k_cache, v_cache, kv_len, scale=None, out=None, max_kv_len=None)``
 * ``decode_attn_gqa_ex(..., num_splits=...)``
 * ``decode_step(q, k_new, v_new, k_cache, v_cache, pos, ...)``: append + decode in one call
+* ``decode_step_rope(q, k_new, v_new, cos, sin, k_cache, v_cache, pos, ...)`` and
+  ``rope_kv_append(q, k_new, v_new, cos, sin, k_cache, v_cache, pos)``: the same
+  with the rotary embedding of the new query and key
 * ``step_graph(layers, pos, max_pos, ...)``: every layer's decode step plus the
   position advance recorded once as a HIP graph (``StepGraph.launch()``)
 * ``decode_partial(q, k_cache, v_cache, kv_len, ...)`` and
   ``decode_combine(workspace, num_splits, out, n_kv_head)``: the two halves
-* ``decode_num_splits``, ``decode_workspace_bytes``, ``device_num_cus``,
- , ``status_string``, ``last_hip_error``, ``abi_version``.
+* ``prefill_append(k_new, v_new, k_cache, v_cache, start)`` and
+  ``prefill_attn_gqa(q, k_cache, v_cache, start, ...)``: prompt prefill
+* ``decode_num_splits``, ``decode_workspace_bytes``, ``prefill_rows_per_workgroup``,
+  ``device_num_cus``, ``status_string``, ``last_hip_error``, ``abi_version``.
 
 There is no fallback: if the library is missing, importing this package
 raises ImportError.
