@@ -1,5 +1,6 @@
-"""GPU parity on seeded random shapes: decode calls and decode steps against
-the fp64 oracle, through the C ABI.
+"""GPU parity on seeded random shapes: decode calls, decode steps and prompt
+prefill (append + causal attention) against the fp64 oracle, through the C
+ABI.
 
 Each case draws batch, KV heads, group size (1..8), capacity, per-row live
 lengths (including 0, 1 and the full capacity), dtype, scale (including 0 and
@@ -99,3 +100,49 @@ def test_random_decode_step(ada, ora, seed):
     assert torch.equal(d["v_cache"].cpu().view(torch.int16), vc.view(torch.int16))
     want = ora.decode(x["q"], kc, vc, [p + 1 for p in pos], scale)
     assert_parity(out, want, dtype, f"random decode step {seed}")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_prefill(ada, ora, seed):
+    """Prompt append then causal prefill attention from random starts
+    (including 0, continued prompts and prompts running past the cache):
+    appended rows bit for bit, outputs within tolerance of the oracle. Slots
+    no token may see hold NaN. Prompt lengths reach past one 64-row block so
+    both workgroup sizes and ragged row tiles occur."""
+    rng = random.Random(7600 + seed)
+    B = rng.choice([1, 2, 3, 4])
+    Hkv = rng.choice([1, 2, 4, 8])
+    G = rng.randint(1, 8)
+    Hq = Hkv * G
+    S = rng.choice([16, 100, 300, 700, 1500])
+    T = rng.randint(1, min(S, 400))
+    dtype = rng.choice(["fp16", "bf16"])
+    scale = rng.choice([float(np.float32(1 / math.sqrt(128)))] * 3 + [0.5, -0.3, 0.0])
+    starts = [rng.choice([0, 0, rng.randint(0, S - 1), S - T // 2]) for _ in range(B)]
+    say(f"case random prefill {seed}: B={B} Hq={Hq} Hkv={Hkv} S={S} T={T} {dtype} starts={starts} scale={scale}")
+    g = torch.Generator().manual_seed(7700 + seed)
+    dt = W.TORCH_DTYPES[dtype]
+    q = torch.randn((B, Hq, T, 128), generator=g).to(dt)
+    kc = torch.randn((B, Hkv, S, 128), generator=g).to(dt)
+    vc = torch.randn((B, Hkv, S, 128), generator=g).to(dt)
+    kn = torch.randn((B, Hkv, T, 128), generator=g).to(dt)
+    vn = torch.randn((B, Hkv, T, 128), generator=g).to(dt)
+    for b, st in enumerate(starts):  # slots past the prompt's end are never visible
+        end = max(0, min(S, st + T))
+        kc[b, :, end:] = float("nan")
+        vc[b, :, end:] = float("nan")
+    d_kc, d_vc = kc.cuda(), vc.cuda()
+    st_t = torch.tensor(starts, dtype=torch.int32, device="cuda")
+    ada.prefill_append(kn.cuda(), vn.cuda(), d_kc, d_vc, st_t)
+    out = ada.prefill_attn_gqa(q.cuda(), d_kc, d_vc, st_t, scale=scale)
+    torch.cuda.synchronize()
+    want_kc, want_vc = kc.clone(), vc.clone()
+    for b, st in enumerate(starts):
+        for t in range(T):
+            if 0 <= st + t < S:
+                want_kc[b, :, st + t] = kn[b, :, t]
+                want_vc[b, :, st + t] = vn[b, :, t]
+    assert torch.equal(d_kc.cpu().view(torch.int16), want_kc.view(torch.int16))
+    assert torch.equal(d_vc.cpu().view(torch.int16), want_vc.view(torch.int16))
+    want = ora.prefill(q, want_kc, want_vc, starts, scale)
+    assert_parity(out, want, dtype, f"random prefill {seed}")
