@@ -106,6 +106,10 @@ constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
 constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each 8
 constexpr int kDppRor8 = 0x128;       // lane i <- lane i^8 within each 16
+constexpr int kDppRowShr1 = 0x111;    // lane i <- lane i-1 within each 16 (none for the first)
+constexpr int kDppRowShr2 = 0x112;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
 
 struct Sum {
   static __device__ __forceinline__ float op(float a, float b) { return a + b; }
@@ -264,17 +268,19 @@ __device__ __forceinline__ uint4 rope_chunk(const uint16_t* row, const uint16_t*
 // live prefix is p + 1 slots. Otherwise lengths come from kv_len, or are
 // max_kv_len for every row when kv_len is NULL (one position for the whole
 // batch: nothing is read before the K/V stream starts).
+// Live slots of a decode step whose new row sits at slot p: p + 1 clamped
+// to [0, max_kv_len], written so that p = INT_MAX does not overflow.
+__device__ __forceinline__ int step_length(int p, int max_kv_len) {
+  return p < 0 ? 0 : (p >= max_kv_len ? max_kv_len : p + 1);
+}
+
 // Live slots of batch row b: pos[b] + 1 for a decode step (pos NULL: all
 // rows at slot max_kv_len - 1), else kv_len[b] (NULL: max_kv_len), clamped
 // to [0, max_kv_len].
 __device__ __forceinline__ int row_length(const int32_t* kv_len, const int32_t* pos, bool step, int max_kv_len,
                                           int b) {
-  int n = max_kv_len;
-  if (step) {
-    n = (pos != nullptr ? pos[b] : max_kv_len - 1) + 1;
-  } else if (kv_len != nullptr) {
-    n = kv_len[b];
-  }
+  if (step) return step_length(pos != nullptr ? pos[b] : max_kv_len - 1, max_kv_len);
+  const int n = kv_len != nullptr ? kv_len[b] : max_kv_len;
   return n < 0 ? 0 : (n > max_kv_len ? max_kv_len : n);
 }
 
@@ -292,13 +298,19 @@ __device__ __forceinline__ unsigned wave_sum_u32(unsigned x) {
 }
 
 // Inclusive prefix sum over the lanes of a wavefront; all lanes active.
+// Row shifts scan each 16-lane row (a lane with no source lane d below it in
+// its row adds 0), then every row adds the totals of the rows before it,
+// read from their last lanes into scalars. No LDS round trip.
 __device__ __forceinline__ unsigned wave_inclusive_scan(unsigned x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const unsigned y = static_cast<unsigned>(__shfl_up(static_cast<int>(x), d, 64));
-    if (lane >= d) x += y;
-  }
-  return x;
+  x += static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kDppRowShr1, 0xF, 0xF, false));
+  x += static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kDppRowShr2, 0xF, 0xF, false));
+  x += static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kDppRowShr4, 0xF, 0xF, false));
+  x += static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), kDppRowShr8, 0xF, 0xF, false));
+  const unsigned r0 = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(x), 15));
+  const unsigned r1 = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(x), 31));
+  const unsigned r2 = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(x), 47));
+  const int row = lane >> 4;
+  return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
 // Balanced split plan for batches whose lengths live on the device (so the
@@ -314,17 +326,23 @@ __device__ __forceinline__ unsigned wave_inclusive_scan(unsigned x, int lane) {
 // lanes active): lane-parallel divisions and cross-lane sums instead of a
 // serial walk over the rows. The host keeps max_kv_len <= 2^25 on this path,
 // so every sum fits in 32 bits. Returns, for the lane's row (zeros for lanes
-// past the batch), its first slot and slot count; the chunk is the same in
-// every lane.
+// past the batch), its first slot and slot count, and for a decode step the
+// slot of its new row; the chunk is the same in every lane.
 struct BalancedRows {
   int chunk;
   int first;  // first workgroup slot of this lane's row
   int count;  // slots of this lane's row
+  int p;      // decode step: pos[lane] (pos NULL: max_kv_len - 1)
 };
 
 __device__ __forceinline__ BalancedRows balanced_rows(const int32_t* kv_len, const int32_t* pos, bool step,
                                                       int max_kv_len, int batch, int slots, int lane) {
-  const unsigned n = lane < batch ? static_cast<unsigned>(row_length(kv_len, pos, step, max_kv_len, lane)) : 0u;
+  int p = max_kv_len - 1;
+  unsigned n = 0;
+  if (lane < batch) {
+    if (step && pos != nullptr) p = pos[lane];
+    n = static_cast<unsigned>(step ? step_length(p, max_kv_len) : row_length(kv_len, pos, false, max_kv_len, lane));
+  }
   const unsigned total = wave_sum_u32(n);
   const unsigned tile = kTileRows;
   auto round_tile = [&](unsigned c) { return c < tile ? tile : (c + tile - 1) / tile * tile; };
@@ -342,7 +360,7 @@ __device__ __forceinline__ BalancedRows balanced_rows(const int32_t* kv_len, con
   }
   const unsigned count = (n + c - 1) / c;
   const unsigned incl = wave_inclusive_scan(count, lane);
-  return {static_cast<int>(c), static_cast<int>(incl - count), static_cast<int>(count)};
+  return {static_cast<int>(c), static_cast<int>(incl - count), static_cast<int>(count), p};
 }
 
 struct SplitRange {
@@ -374,7 +392,9 @@ __device__ __forceinline__ bool begin_split(SplitRange& r, uint16_t* k_cache, ui
   int split = blockIdx.x;
   int b = blockIdx.z;
   size_t slot = static_cast<size_t>(split) * gridDim.z + b;  // partial slot (split-major)
-  if (chunk == 0) {
+  int p_dev = 0;  // under the balanced plan: pos[b], already read by lane b
+  const bool balanced = chunk == 0;
+  if (balanced) {
     // Balanced plan: this workgroup is slot z * splits + x of its KV head;
     // its row is the one whose slot range holds it.
     const int idx = blockIdx.z * gridDim.x + blockIdx.x;
@@ -385,15 +405,16 @@ __device__ __forceinline__ bool begin_split(SplitRange& r, uint16_t* k_cache, ui
     const unsigned long long hit =
         __ballot(lane < static_cast<int>(gridDim.z) && idx >= rows.first && idx < rows.first + rows.count);
     if (hit == 0) return false;  // a slot no row needs: nothing to write
-    b = __ffsll(hit) - 1;
-    split = idx - __shfl(rows.first, b, 64);
+    b = __ffsll(hit) - 1;  // uniform: lane reads below need no LDS round trip
+    split = idx - __builtin_amdgcn_readlane(rows.first, b);
+    p_dev = __builtin_amdgcn_readlane(rows.p, b);
     slot = idx;
   }
   r.head_off = (static_cast<size_t>(b) * n_kv_head + g) * static_cast<size_t>(capacity) * D;
   r.new_row = (static_cast<size_t>(b) * n_kv_head + g) * D;
   r.p_new = -1;
   if (k_new != nullptr) {
-    r.p_new = pos != nullptr ? pos[b] : max_kv_len - 1;
+    r.p_new = pos == nullptr ? max_kv_len - 1 : (balanced ? p_dev : pos[b]);
     if (split == 0 && tid < 32 && r.p_new >= 0 && r.p_new < capacity) {
       const int c = 8 * (tid & 15);  // one 16-byte chunk of the key (tid < 16) or value row
       const size_t dst = r.head_off + static_cast<size_t>(r.p_new) * D + c;
@@ -405,13 +426,12 @@ __device__ __forceinline__ bool begin_split(SplitRange& r, uint16_t* k_cache, ui
       }
     }
   }
-  int n = max_kv_len;
   if (k_new != nullptr) {
-    n = r.p_new + 1;
-  } else if (kv_len != nullptr) {
-    n = kv_len[b];
+    r.n = step_length(r.p_new, max_kv_len);
+  } else {
+    const int n = kv_len != nullptr ? kv_len[b] : max_kv_len;
+    r.n = n < 0 ? 0 : (n > max_kv_len ? max_kv_len : n);
   }
-  r.n = n < 0 ? 0 : (n > max_kv_len ? max_kv_len : n);
   const int nsplit = (r.n + chunk - 1) / chunk;  // splits holding live slots
   const size_t head_row0 = static_cast<size_t>(b) * n_head + static_cast<size_t>(g) * G;
   r.out_row0 = head_row0 * D;
@@ -794,8 +814,8 @@ __global__ __launch_bounds__(64 * kMaxGroup) void combine_kernel(
   if (balanced) {
     const int slots = num_splits * static_cast<int>(gridDim.y);
     const BalancedRows rows = balanced_rows(kv_len, pos, step != 0, max_kv_len, gridDim.y, slots, lane);
-    const int first = __shfl(rows.first, b, 64);
-    num_splits = __shfl(rows.count, b, 64);
+    const int first = __builtin_amdgcn_readlane(rows.first, b);
+    num_splits = __builtin_amdgcn_readlane(rows.count, b);
     row0 = static_cast<uint32_t>(first) * n_head + static_cast<uint32_t>(g) * group + i;
     split_stride = n_head;
   }

@@ -483,10 +483,12 @@ def test_decode_step_positions_past_the_host_bound(ada, ora, rope):
     positions write nothing and give zeros; positions past the cache write
     nothing. Equal, bit for bit, to the append (or rotary append) followed by
     the decode with kv_len = min(pos, max_pos) + 1, for per-row, balanced and
-    one-split plans."""
-    B, Hq, Hkv, D, S, dtype = 5, 32, 8, 128, 2048, "bf16"
+    one-split plans. The extreme int32 positions take the same rules (the
+    largest attends over max_pos + 1 slots: pos + 1 must not wrap)."""
+    B, Hq, Hkv, D, S, dtype = 7, 32, 8, 128, 2048, "bf16"
     max_pos = 1000
-    pos = [1000, 1500, 2047, -1, 2048]  # at, past the bound (twice), negative, past the cache
+    # at, past the bound (twice), negative, past the cache, int32 extremes
+    pos = [1000, 1500, 2047, -1, 2048, 2**31 - 1, -2**31]
     for k, splits in enumerate((0, 1, 3)):
         say(f"case decode step past max_pos rope={rope} pos={pos} max_pos={max_pos} splits={splits}")
         lens = [min(S, max(0, p)) for p in pos]
@@ -513,6 +515,8 @@ def test_decode_step_positions_past_the_host_bound(ada, ora, rope):
         assert torch.equal(d1["v_cache"].view(torch.int16), d2["v_cache"].view(torch.int16)), "value rows differ"
         assert torch.equal(fused, ref), "decode step differs from append + decode"
         assert torch.count_nonzero(fused[3]) == 0, "a negative position must give a zero row"
+        assert torch.count_nonzero(fused[6]) == 0, "a negative position must give a zero row"
+        assert torch.count_nonzero(fused[5]) > 0, "the largest position attends over max_pos + 1 slots"
         if not rope:
             kc, vc = ora.kv_append(kn, vn, x["k_cache"], x["v_cache"], pos)
             to16 = lambda a: torch.from_numpy(a.view(np.int16)).view(W.TORCH_DTYPES[dtype])
