@@ -273,7 +273,9 @@ def test_split_invariance_and_determinism(ada, ora):
 
 
 def test_workspace_reuse_across_split_counts(ada, ora):
-    """The cached workspace's arrival counters are left ready by every call."""
+    """One cached workspace serves calls with different split counts in turn
+    (it needs no preparation: every partial a combine reads is written by the
+    partial launch before it)."""
     shp = shape(4, 32, 8, 2048, "fp16")
     for k, splits in enumerate((7, 3, 0, 2, 31, 0, 1, 5)):
         lens = W.ragged_lengths(4, 1, 2048, 800 + k)
