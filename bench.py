@@ -304,6 +304,54 @@ def time_s2pro_run(ada, device) -> dict:
             "GBs": round(nbytes / (run_ms * 1e-3) / 1e9, 1), "splits": splits}
 
 
+def time_minicpm_sweep(ada, device, layers: int = 4) -> dict:
+    """The MiniCPM-shaped lockstep sweep (batch 4, 32/8 heads, bf16, capacity
+    8192; VoxCPM #395, section 6.3): position_id swept 0..8191, each step
+    appending the new rows at slot p and attending over p + 1 slots. One
+    library step graph holds ``layers`` layers (separate caches, together
+    above the 256 MB Infinity Cache, so the reads come from HBM) and the
+    device-side position advance; one replay per position, 8192 replays.
+    The launches are sized for the last slot (max_pos 8191) and the positions
+    live on the device, so the balanced plan spreads each step's rows over
+    the splits."""
+    shp = W.WORKLOADS["minicpm_stream"].shape
+    B, Hq, Hkv, D, S = shp.batch, shp.n_head, shp.n_kv_head, shp.head_dim, shp.capacity
+    L = layers
+    dt = W.TORCH_DTYPES[shp.dtype]
+    kc = torch.empty((L, B, Hkv, S, D), dtype=dt, device=device)
+    vc = torch.empty_like(kc)
+    for layer in range(L):
+        x = W.decode_inputs(shp, [S] * B, W.seed_for(3, 80_000 + layer), device=device, tail="random")
+        kc[layer].copy_(x["k_cache"])
+        vc[layer].copy_(x["v_cache"])
+        del x
+    k_new = W.randn16((L, B, Hkv, D), shp.dtype, W.seed_for(3, 81_000), device=device)
+    v_new = W.randn16((L, B, Hkv, D), shp.dtype, W.seed_for(3, 81_001), device=device)
+    q = W.randn16((L, B, Hq, D), shp.dtype, W.seed_for(3, 81_002), device=device)
+    out = torch.empty((L, B, Hq, D), dtype=dt, device=device)
+    pos = torch.zeros((B,), dtype=torch.int32, device=device)
+    splits = ada.decode_num_splits(B, Hq, Hkv, S)
+    ws = ada.new_workspace(ada.decode_workspace_bytes(B, Hq, Hkv, D, max(2, splits)), device)
+    graph = ada.step_graph([(q[i], k_new[i], v_new[i], kc[i], vc[i], out[i]) for i in range(L)], pos, S - 1,
+                           scale=1.0 / math.sqrt(D), workspace=ws)
+    graph.launch()  # warm-up replay
+    pos.zero_()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(S):
+        graph.launch()
+    torch.cuda.synchronize()
+    run_ms = (time.perf_counter() - t0) * 1e3
+    graph.close()
+    nbytes = L * sum(decode_bytes(B, Hq, Hkv, D, [p + 1] * B) for p in range(S))
+    del kc, vc
+    return {"workload": f"minicpm lockstep sweep: batch 4, 32/8 heads, head_dim 128, bf16, capacity 8192, positions "
+                        f"0..8191, {L} layers (one decode step each) per graph replay",
+            "run_ms": round(run_ms, 2), "us_per_layer_call": round(run_ms * 1e3 / (S * L), 2), "run_bytes": nbytes,
+            "GBs": round(nbytes / (run_ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (run_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "splits": splits}
+
+
 def time_full_vs_active(ada, device, iters: int = 20) -> dict:
     """The pages' experiment restated on this kernel (fish-speech #1310,
     "CUDA benchmark"; VoxCPM #395, section 6.3): a decode call that attends
@@ -617,6 +665,7 @@ def main(argv=None):
         also["s2pro_run"] = time_s2pro_run(ada, device)
         also["full_capacity_vs_active_prefix"] = time_full_vs_active(ada, device)
         also["minicpm_stream"] = time_minicpm_stream(ada, device)
+        also["minicpm_sweep"] = time_minicpm_sweep(ada, device)
         also["rope_step"] = time_rope_step(ada, device)
         also["prefill"] = time_prefill(ada, device)
 
