@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import assert_parity
+from parity import assert_parity, assert_parity_bound, prefill_bound
 
 pytestmark = pytest.mark.gpu
 
@@ -106,7 +106,8 @@ def test_random_decode_step(ada, ora, seed):
 def test_random_prefill(ada, ora, seed):
     """Prompt append then causal prefill attention from random starts
     (including 0, continued prompts and prompts running past the cache):
-    appended rows bit for bit, outputs within tolerance of the oracle. Slots
+    appended rows bit for bit, outputs within the prefill's derived bound
+    (tests/parity.py, prefill_bound) and relative Frobenius tolerance. Slots
     no token may see hold NaN. Prompt lengths reach past one 64-row block so
     both workgroup sizes and ragged row tiles occur."""
     rng = random.Random(7600 + seed)
@@ -145,4 +146,5 @@ def test_random_prefill(ada, ora, seed):
     assert torch.equal(d_kc.cpu().view(torch.int16), want_kc.view(torch.int16))
     assert torch.equal(d_vc.cpu().view(torch.int16), want_vc.view(torch.int16))
     want = ora.prefill(q, want_kc, want_vc, starts, scale)
-    assert_parity(out, want, dtype, f"random prefill {seed}")
+    lens = [[max(0, min(S, st + t + 1)) for t in range(T)] for st in starts]
+    assert_parity_bound(out, want, prefill_bound(want, want_vc, lens, dtype), dtype, f"random prefill {seed}")
