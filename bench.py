@@ -252,6 +252,67 @@ def time_long_context(ada, device, iters: int = 20) -> dict:
             "call_frac_of_peak": round(nbytes / whole / 1e3 / PEAK_HBM_GBS, 4)}
 
 
+def time_shards(ada, device, iters: int = 20) -> dict:
+    """One GPU's share of the long-context workload under two 8-way splits
+    (the exchange between GPUs is not measured here): (a) KV heads over 8
+    GPUs -- batch 8, 4 query heads sharing 1 KV head, kv_len 32768, one whole
+    decode call; (b) the sequence over 8 GPUs -- each holds 4096 slots of
+    every (batch row, KV head) and runs the partial kernel on them, then,
+    once the partials are all-gathered, one combine over 8x its own split
+    count (timed on partials of the same size)."""
+    wl = W.WORKLOADS["long_context"]
+    shp = wl.shape
+    B, Hq, Hkv, D, S = shp.batch, shp.n_head, shp.n_kv_head, shp.head_dim, shp.capacity
+    scale = 1.0 / math.sqrt(D)
+
+    def timed(fn):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(SPIN_CYCLES)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / iters
+
+    res = {}
+    tp = W.DecodeShape(B, Hq // 8, Hkv // 8, D, S, shp.dtype)
+    x = W.decode_inputs(tp, [S] * B, W.seed_for(4, 90_000), device=device, tail="random",
+                        outlier_p=wl.outlier_p, outlier_scale=wl.outlier_scale)
+    splits = ada.decode_num_splits(B, tp.n_head, tp.n_kv_head, S)
+    ws = ada.new_workspace(ada.decode_workspace_bytes(B, tp.n_head, tp.n_kv_head, D, max(2, splits)), device)
+    out = torch.empty_like(x["q"])
+    us = timed(lambda: ada.decode_attn_gqa(x["q"], x["k_cache"], x["v_cache"], None, scale=scale, out=out,
+                                           max_kv_len=S, workspace=ws))
+    nb = decode_bytes(B, tp.n_head, tp.n_kv_head, D, [S] * B)
+    res["kv_heads_over_8"] = {"shape": "batch 8, 4/1 heads, kv_len 32768, bf16", "splits": splits,
+                              "call_us": round(us, 2), "GBs": round(nb / us / 1e3, 1),
+                              "frac_of_peak": round(nb / us / 1e3 / PEAK_HBM_GBS, 4)}
+    del x
+    n = S // 8
+    sp = W.DecodeShape(B, Hq, Hkv, D, n, shp.dtype)
+    x = W.decode_inputs(sp, [n] * B, W.seed_for(4, 90_001), device=device, tail="random",
+                        outlier_p=wl.outlier_p, outlier_scale=wl.outlier_scale)
+    local = ada.decode_num_splits(B, Hq, Hkv, n)
+    ws = ada.new_workspace(ada.decode_workspace_bytes(B, Hq, Hkv, D, 8 * local), device)
+    out = torch.empty_like(x["q"])
+    part = timed(lambda: ada.decode_partial(x["q"], x["k_cache"], x["v_cache"], None, scale=scale, max_kv_len=n,
+                                            workspace=ws))
+    ada.decode_partial(x["q"], x["k_cache"], x["v_cache"], None, scale=scale, max_kv_len=n,
+                       num_splits=8 * local, workspace=ws)
+    comb = timed(lambda: ada.decode_combine(ws, 8 * local, out, Hkv))
+    nb = decode_bytes(B, Hq, Hkv, D, [n] * B)
+    res["sequence_over_8"] = {"shape": "batch 8, 32/8 heads, 4096 of 32768 slots per GPU, bf16",
+                              "local_splits": local, "partial_us": round(part, 2),
+                              "partial_GBs": round(nb / part / 1e3, 1),
+                              "combine_us_over_8x_splits": round(comb, 2),
+                              "partial_bytes_per_gpu_to_gather": B * Hq * local * (D + 2) * 4}
+    del x
+    return res
+
+
 def time_s2pro_run(ada, device) -> dict:
     """The S2-Pro-shaped run (36 layers, 32/8 heads, fp16, capacity 32768,
     prefill 234, then 1024 decode steps): one HIP graph holds a whole decode
@@ -662,6 +723,7 @@ def main(argv=None):
             "eager_GBs": round(sweep.step_bytes / (eager_ms * 1e-3) / 1e9, 1)}
     if not args.no_long_context:
         also["long_context"] = time_long_context(ada, device)
+        also["shards"] = time_shards(ada, device)
         also["s2pro_run"] = time_s2pro_run(ada, device)
         also["full_capacity_vs_active_prefix"] = time_full_vs_active(ada, device)
         also["minicpm_stream"] = time_minicpm_stream(ada, device)
