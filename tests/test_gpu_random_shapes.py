@@ -148,3 +148,23 @@ def test_random_prefill(ada, ora, seed):
     want = ora.prefill(q, want_kc, want_vc, starts, scale)
     lens = [[max(0, min(S, st + t + 1)) for t in range(T)] for st in starts]
     assert_parity_bound(out, want, prefill_bound(want, want_vc, lens, dtype), dtype, f"random prefill {seed}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_rope_step(ada, ora, seed):
+    """Rotary decode steps (ada_decode_step_rope) on random shapes and
+    per-row positions -- including 0, the last slot, negative and past the
+    cache -- with heuristic (balanced for several rows) or forced splits:
+    rotated key rows bit for bit, outputs within tolerance of the oracle
+    (oracle/rope.py composed with the append and decode oracles)."""
+    from test_gpu_rope import rope_step_case
+
+    rng = random.Random(7800 + seed)
+    B = rng.choice([1, 2, 3, 4, 6])
+    Hkv = rng.choice([1, 2, 4, 8])
+    G = rng.randint(1, 8)
+    S = rng.choice([64, 65, 300, 1000, 2049])
+    pos = [rng.choice([0, S - 1, rng.randint(0, S - 1), rng.randint(0, S - 1), -1, S]) for _ in range(B)]
+    dtype = rng.choice(["fp16", "bf16"])
+    splits = rng.choice([0, 0, 1, 3, 16])
+    rope_step_case(ada, ora, B, Hkv * G, Hkv, S, dtype, pos, 7900 + 10 * seed, splits)
