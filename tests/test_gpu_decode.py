@@ -199,6 +199,37 @@ def test_long_context(ada, ora):
         assert_parity(out[b:b + 1], want, "bf16", f"long context row {b}")
 
 
+def test_large_capacity(ada, ora):
+    """Caches of 2^22 slots per (batch row, KV head), 3 GiB each for K and V:
+    slot offsets past 2^31 bytes, the heuristic's cap of 256 splits
+    (16384-slot ranges, so the combine merges 8 batches of 32 partials), a
+    ragged short row beside full ones (device lengths: the balanced plan), and
+    a decode step with per-row positions at the end. Inputs drawn on the GPU;
+    the oracle computes every row."""
+    S = 1 << 22
+    B = 3
+    shp = shape(B, 2, 1, S, "bf16")
+    lens = [S, 77, S - 5]
+    say(f"case large capacity: S={S} lens={lens}: generating on the GPU")
+    x = W.decode_inputs(shp, lens, 7300, device="cuda", tail="nan")
+    assert ada.decode_num_splits(B, 2, 1, S) == 256
+    out = ada.decode_attn_gqa(x["q"], x["k_cache"], x["v_cache"], x["kv_len"], scale=SCALE, max_kv_len=S)
+    torch.cuda.synchronize()
+    q, kc, vc = x["q"].cpu(), x["k_cache"].cpu(), x["v_cache"].cpu()
+    assert_parity(out, ora.decode(q, kc, vc, lens, SCALE), "bf16", "large capacity")
+    pos = [S - 1, 77, S - 5]
+    kn, vn = W.append_inputs(B, 1, 128, "bf16", 7301)
+    pos_t = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    step = ada.decode_step(x["q"], kn.cuda(), vn.cuda(), x["k_cache"], x["v_cache"], pos_t, scale=SCALE)
+    torch.cuda.synchronize()
+    for b, p_ in enumerate(pos):
+        kc[b, :, p_] = kn[b]
+        vc[b, :, p_] = vn[b]
+        got_k = x["k_cache"][b, :, p_].cpu()
+        assert torch.equal(got_k.view(torch.int16), kn[b].view(torch.int16)), f"key row of batch row {b}"
+    assert_parity(step, ora.decode(q, kc, vc, [p_ + 1 for p_ in pos], SCALE), "bf16", "large capacity step")
+
+
 # ---------------------------------------------------------------------------
 # Grouped-query sizes, ragged batches and edges.
 
