@@ -55,12 +55,13 @@
 //     keys.
 //   * Row statistics move from the score layout (row = lane % 16) to the
 //     output layout (rows 4 * (lane / 16) + j) with ds_bpermute.
-//   * LDS traffic is what bounds the kernel (on MI355X, removing the LDS
-//     operand reads and tile stores made an earlier version 44 % faster,
+//   * LDS traffic bounded an earlier, register-staged version (on MI355X,
+//     removing its LDS operand reads and tile stores made it 44 % faster,
 //     removing either matrix product or the softmax 7-12 %). With RB = 2
 //     each K and V operand read serves two row blocks, halving the LDS bytes
-//     per matrix instruction; RB = 1 is for launches too small to fill the
-//     device with 128-row workgroups (prefill_rows_per_workgroup decides).
+//     per matrix instruction, and the LDS now runs at about 40 % of its
+//     bandwidth; RB = 1 is for launches too small to fill the device with
+//     128-row workgroups (prefill_rows_per_workgroup decides).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
