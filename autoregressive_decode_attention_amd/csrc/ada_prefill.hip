@@ -39,14 +39,15 @@
 //     more than 2^8, so the weights exp2(|scale| s - m) <= 256 need one FMA
 //     and one exp each. A negative scale is applied as |scale| to the
 //     negated query (an exact sign flip), which keeps the largest raw score
-//     the largest scaled one. The weights are rounded once to the 16-bit
-//     type, two per conversion, and the row sums add the rounded weights (a
-//     dot with ones), so numerator and denominator see the same values.
-//     Keys past a row's causal limit are masked only on the tiles that
-//     reach it.
-//   * O += P V with the same instruction: P is the A operand straight from
-//     registers, its K index running over the lane's 8 keys of a 32-key step
-//     (a fixed permutation of the keys, the same one the V operand uses).
+//     the largest scaled one. The weights stay fp32 in effect: each becomes
+//     a pair of 16-bit values hi = rnd(p), lo = rnd(p - hi), two per
+//     conversion, and the row sums add both (a dot with ones), so numerator
+//     and denominator see the same values. Keys past a row's causal limit
+//     are masked only on the tiles that reach it.
+//   * O += P V with the same instruction, once for the hi and once for the
+//     lo weights: P is the A operand straight from registers, its K index
+//     running over the lane's 8 keys of a 32-key step (a fixed permutation
+//     of the keys, the same one the V operand uses).
 //     V stays row-major and is read with the transposing LDS read
 //     (ds_read_b64_tr_b16): within each 16-lane group, lane s addresses key
 //     row r + s / 4 at dims 4 * (s % 4) .. + 3 of a 16-dim block, and lane d
@@ -91,10 +92,20 @@ struct PF16 {
   static __device__ __forceinline__ uint32_t pack(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), h2));
   }
+  // The two packed values, exactly, as fp32.
+  static __device__ __forceinline__ void unpack(uint32_t w, float& a, float& b) {
+    const h2 h = __builtin_bit_cast(h2, w);
+    a = static_cast<float>(h.x);
+    b = static_cast<float>(h.y);
+  }
   // c plus both packed values (a dot with (1, 1): exact products, fp32 sum).
   static __device__ __forceinline__ float sum2(uint32_t w, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, w), __builtin_bit_cast(h2, 0x3C003C00u), c, false);
   }
+  // Base-2 exponent added to every softmax weight (and so to the row sums,
+  // which cancels): weights up to 2^15 still fit fp16, and the low parts of
+  // the weight pairs stay in fp16's normal range down to weights of 2^-3.
+  static constexpr float kWeightExp = 7.0f;
 };
 
 struct PBF16 {
@@ -107,9 +118,14 @@ struct PBF16 {
   static __device__ __forceinline__ uint32_t pack(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{a, b}), bh2));
   }
+  static __device__ __forceinline__ void unpack(uint32_t w, float& a, float& b) {
+    a = __uint_as_float(w << 16);
+    b = __uint_as_float(w & 0xffff0000u);
+  }
   static __device__ __forceinline__ float sum2(uint32_t w, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bh2, w), __builtin_bit_cast(bh2, 0x3F803F80u), c, false);
   }
+  static constexpr float kWeightExp = 0.0f;  // bf16 has fp32's exponent range
 };
 
 constexpr int D = kHeadDim;     // 128
@@ -186,12 +202,19 @@ __device__ __forceinline__ void tile_scores(const uint4* sk, const uint4 (&qb)[R
 // Online softmax of one tile's scores (keys base .. base + 63). FULL: every
 // key is within every row's causal limit, so nothing is masked. Moves the
 // running reference m_run (rescaling o and l_run) when a row's maximum
-// passes it by more than 2^8, adds the tile's weights to l_run and leaves
-// them, rounded to 16 bits, in pa as the A operand of the P V product.
+// passes it by more than 2^8 and adds the tile's weights to l_run.
+//
+// The weights reach the P V product on the matrix cores, whose A operand is
+// 16-bit, as a pair: hi = rnd16(p) in ph and lo = rnd16(p - hi) in pl (p - hi
+// is exact in fp32), and the product is taken with both. hi + lo holds p to
+// a relative 2^-16 (bf16) or 2^-22 (fp16), so the weighted sum sees the fp32
+// softmax weights, not weights rounded to 16 bits (whose 2^-9 relative error
+// in bf16 moves an output by up to 2^-9 times the spread of the value rows
+// it averages). The row sums add the same pairs.
 template <class E, int RB, bool FULL>
 __device__ __forceinline__ void tile_softmax(const f4 (&s)[RB][4], int base, const int (&my_n)[RB], int a,
                                              float cscale, float (&m_run)[RB], float (&l_run)[RB], f4 (&o)[RB][8],
-                                             uint4 (&pa)[RB][2]) {
+                                             uint4 (&ph)[RB][2], uint4 (&pl)[RB][2]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     bool ok[4][4];
@@ -221,10 +244,10 @@ __device__ __forceinline__ void tile_softmax(const f4 (&s)[RB][4], int base, con
         for (int j = 0; j < 4; ++j) o[rb][db][j] *= al[j];
       }
     }
-    const float nref = -finite_ref(m_run[rb]);
+    const float nref = E::kWeightExp - finite_ref(m_run[rb]);
 #pragma unroll
     for (int ks2 = 0; ks2 < 2; ++ks2) {
-      uint32_t w[4];
+      uint32_t wh[4], wl[4];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int nb = 2 * ks2 + h;
@@ -236,19 +259,27 @@ __device__ __forceinline__ void tile_softmax(const f4 (&s)[RB][4], int base, con
             p0 = ok[nb][2 * jj] ? p0 : 0.0f;
             p1 = ok[nb][2 * jj + 1] ? p1 : 0.0f;
           }
-          w[2 * h + jj] = E::pack(p0, p1);
-          l_run[rb] = E::sum2(w[2 * h + jj], l_run[rb]);
+          const uint32_t hi = E::pack(p0, p1);
+          float h0, h1;
+          E::unpack(hi, h0, h1);
+          const uint32_t lo = E::pack(p0 - h0, p1 - h1);
+          wh[2 * h + jj] = hi;
+          wl[2 * h + jj] = lo;
+          l_run[rb] = E::sum2(lo, E::sum2(hi, l_run[rb]));
         }
       }
-      pa[rb][ks2] = make_uint4(w[0], w[1], w[2], w[3]);
+      ph[rb][ks2] = make_uint4(wh[0], wh[1], wh[2], wh[3]);
+      pl[rb][ks2] = make_uint4(wl[0], wl[1], wl[2], wl[3]);
     }
   }
 }
 
-// O += P V over one tile for RB row blocks. V stays row-major in LDS and is
-// read with the transposing LDS read; each V operand serves all RB blocks.
+// O += P V over one tile for RB row blocks, P given as the pair hi + lo. V
+// stays row-major in LDS and is read with the transposing LDS read; each V
+// operand serves both halves of all RB blocks.
 template <class E, int RB>
-__device__ __forceinline__ void tile_pv(const uint4* sv, const uint4 (&pa)[RB][2], int lr, int a, f4 (&o)[RB][8]) {
+__device__ __forceinline__ void tile_pv(const uint4* sv, const uint4 (&ph)[RB][2], const uint4 (&pl)[RB][2], int lr,
+                                        int a, f4 (&o)[RB][8]) {
   const uint16_t* sv16 = reinterpret_cast<const uint16_t*>(sv);
 #pragma unroll
   for (int ks2 = 0; ks2 < 2; ++ks2) {
@@ -266,7 +297,7 @@ __device__ __forceinline__ void tile_pv(const uint4* sv, const uint4 (&pa)[RB][2
       const uint2 w1 = __builtin_bit_cast(uint2, v1);
       const uint4 vop = make_uint4(w0.x, w0.y, w1.x, w1.y);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o[rb][db] = E::mma(pa[rb][ks2], vop, o[rb][db]);
+      for (int rb = 0; rb < RB; ++rb) o[rb][db] = E::mma(pl[rb][ks2], vop, E::mma(ph[rb][ks2], vop, o[rb][db]));
     }
   }
 }
@@ -390,10 +421,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint16_t* __restr
   // wavefront (no causal mask on this tile).
   auto compute = [&](int tile, const uint4* sk, const uint4* sv, auto full_tile) __attribute__((always_inline)) {
     f4 s[RB][4];
-    uint4 pa[RB][2];
+    uint4 ph[RB][2], pl[RB][2];
     tile_scores<E, RB>(sk, qb, lr, a, s);
-    tile_softmax<E, RB, decltype(full_tile)::value>(s, tile * kKeys, my_n, a, cscale, m_run, l_run, o, pa);
-    tile_pv<E, RB>(sv, pa, lr, a, o);
+    tile_softmax<E, RB, decltype(full_tile)::value>(s, tile * kKeys, my_n, a, cscale, m_run, l_run, o, ph, pl);
+    tile_pv<E, RB>(sv, ph, pl, lr, a, o);
   };
 
   // Tiles wholly below the wavefront's smallest causal limit take the

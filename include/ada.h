@@ -305,9 +305,11 @@ int ada_prefill_append(const void* k_new, const void* v_new, void* k_cache, void
  * n = clamp(start[b] + t + 1, 0, capacity):
  *   out[b,h,t,:] = softmax_j(scale * q[b,h,t,:] . K[b,g,j,:]) V[b,g,j,:], j < n
  * and n == 0 gives zeros. Scores and softmax statistics in fp32 (16-bit
- * products are exact), softmax weights rounded once to the dtype for the
- * weighted sum (the row sums use the same rounded weights), output rounded to
- * nearest even.
+ * products are exact; [DECODE-FASTPATH] "Proposed implementation" asks for
+ * fp32 softmax accumulation). The weighted sum runs on the matrix cores with
+ * each fp32 weight split into two 16-bit values, hi = rnd(p) and
+ * lo = rnd(p - hi), so the weights keep 16 (bf16) or 22 (fp16) significant
+ * bits; the row sums add the same pairs. Output rounded to nearest even.
  *
  *   q, out     device, [batch, n_head, q_len, head_dim] (the head-major query
  *              of an SDPA call); out must not overlap the inputs.

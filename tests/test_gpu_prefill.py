@@ -7,11 +7,9 @@ decoding by attending only to the active KV-cache prefix", section 2:
 kv_len = T after the prompt) and [FORWARD-STEP] (VoxCPM #395, "MiniCPM4
 MiniCPMAttention.forward_step Attention Performance Fix", section 5: the
 batch prefill path keeps is_causal=True): token t at position start + t sees
-cache slots 0 .. start + t. Tolerances: the decode's relative Frobenius bound
-(1e-3 fp16, 4e-3 bf16) and, element by element, the bound derived from the
-prefill's arithmetic (16-bit softmax weights in the value product, then one
-output rounding; tests/parity.py, prefill_bound); cache slots no token may
-see hold NaN.
+cache slots 0 .. start + t. Tolerances: those of the decode (max-abs 4e-3 /
+relative Frobenius 1e-3 for fp16, 1.6e-2 / 4e-3 for bf16, over the whole
+output of a call); cache slots no token may see hold NaN.
 """
 import math
 
@@ -21,7 +19,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import assert_parity, assert_parity_bound, prefill_bound
+from parity import assert_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -61,14 +59,8 @@ def prefill_inputs(B, Hq, Hkv, T, S, dtype, starts, seed):
     return q, k, v
 
 
-def visible_lens(starts, T, S):
-    """[B, T] slots token t of each row sees: start + t + 1 clamped to [0, S]."""
-    return [[max(0, min(S, st + t + 1)) for t in range(T)] for st in starts]
-
-
-def check_prefill(out, want, v, starts, dtype, what):
-    T, S = want.shape[2], v.shape[2]
-    return assert_parity_bound(out, want, prefill_bound(want, v, visible_lens(starts, T, S), dtype), dtype, what)
+def check_prefill(out, want, dtype, what):
+    return assert_parity(out, want, dtype, what)
 
 
 def run_prefill(ada, ora, B, Hq, Hkv, T, S, dtype, starts, seed, what=""):
@@ -79,7 +71,7 @@ def run_prefill(ada, ora, B, Hq, Hkv, T, S, dtype, starts, seed, what=""):
     out = ada.prefill_attn_gqa(q.cuda(), k.cuda(), v.cuda(), st, scale=scale)
     torch.cuda.synchronize()
     want = ora.prefill(q, k, v, starts, scale)
-    check_prefill(out, want, v, starts, dtype, what)
+    check_prefill(out, want, dtype, what)
     return q, k, v, out
 
 
@@ -163,8 +155,7 @@ def test_prefill_full_size_sampled(ada, ora, dtype):
     got = out.cpu()
     for t in (0, 1, 15, 16, 31, 32, 63, 64, 127, 1000, 2047, 2048, 3071, 4094, 4095):
         want = ora.decode(q[:, :, t, :].contiguous(), k, v, [t + 1], scale).reshape(B, Hq, 1, 128)
-        bound = prefill_bound(want, v, [[t + 1]], dtype)
-        assert_parity_bound(got[:, :, t:t + 1, :], want, bound, dtype, f"token {t}")
+        assert_parity(got[:, :, t:t + 1, :], want, dtype, f"token {t}")
 
 
 def test_prefill_rows_match_decode(ada):
@@ -199,7 +190,7 @@ def test_prefill_then_decode_pipeline(ada, ora):
     kc2, vc2 = ora.prefill_append(kn, vn, kc, vc, [0])
     to16 = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.float16)
     assert np.array_equal(bits(kd), kc2)
-    check_prefill(out, ora.prefill(q, to16(kc2), to16(vc2), [0], 1 / math.sqrt(128)), to16(vc2), [0], "fp16", "prompt")
+    check_prefill(out, ora.prefill(q, to16(kc2), to16(vc2), [0], 1 / math.sqrt(128)), "fp16", "prompt")
     for i in range(3):
         qs = torch.randn((B, Hq, 128), generator=g).half()
         kns = torch.randn((B, Hkv, 128), generator=g).half()
@@ -220,4 +211,4 @@ def test_prefill_scale_edges(ada, ora):
         out = ada.prefill_attn_gqa(q.cuda(), k.cuda(), v.cuda(), torch.tensor([0, 60], dtype=torch.int32,
                                                                                device="cuda"), scale=scale)
         torch.cuda.synchronize()
-        check_prefill(out, ora.prefill(q, k, v, [0, 60], scale), v, [0, 60], dtype, f"scale {scale}")
+        check_prefill(out, ora.prefill(q, k, v, [0, 60], scale), dtype, f"scale {scale}")

@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import workloads as W
-from parity import assert_parity, assert_parity_bound, prefill_bound
+from parity import assert_parity
 
 pytestmark = pytest.mark.gpu
 
@@ -106,10 +106,27 @@ def test_random_decode_step(ada, ora, seed):
 def test_random_prefill(ada, ora, seed):
     """Prompt append then causal prefill attention from random starts
     (including 0, continued prompts and prompts running past the cache):
-    appended rows bit for bit, outputs within the prefill's derived bound
-    (tests/parity.py, prefill_bound) and relative Frobenius tolerance. Slots
+    appended rows bit for bit, outputs within the decode's tolerances. Slots
     no token may see hold NaN. Prompt lengths reach past one 64-row block so
     both workgroup sizes and ragged row tiles occur."""
+    random_prefill_case(ada, ora, seed)
+
+
+# Draws of the case above (beyond the committed seeds) on which softmax
+# weights rounded once to bf16 in the value product would miss the bf16
+# max-abs: a CPU model of that arithmetic (exact weights rounded to nearest
+# even, the row sums of the rounded weights, output rounded) puts their
+# largest error at 1.5e-2 .. 1.6e-2 of the 1.6e-2 bar. The kernel carries
+# each weight as a pair of 16-bit values, so these must pass with margin.
+WEIGHT_ROUNDING_SEEDS = (26, 250, 485, 676, 913, 918, 922)
+
+
+@pytest.mark.parametrize("seed", WEIGHT_ROUNDING_SEEDS)
+def test_random_prefill_weight_rounding(ada, ora, seed):
+    random_prefill_case(ada, ora, seed)
+
+
+def random_prefill_case(ada, ora, seed):
     rng = random.Random(7600 + seed)
     B = rng.choice([1, 2, 3, 4])
     Hkv = rng.choice([1, 2, 4, 8])
@@ -146,8 +163,7 @@ def test_random_prefill(ada, ora, seed):
     assert torch.equal(d_kc.cpu().view(torch.int16), want_kc.view(torch.int16))
     assert torch.equal(d_vc.cpu().view(torch.int16), want_vc.view(torch.int16))
     want = ora.prefill(q, want_kc, want_vc, starts, scale)
-    lens = [[max(0, min(S, st + t + 1)) for t in range(T)] for st in starts]
-    assert_parity_bound(out, want, prefill_bound(want, want_vc, lens, dtype), dtype, f"random prefill {seed}")
+    assert_parity(out, want, dtype, f"random prefill {seed}")
 
 
 @pytest.mark.parametrize("seed", range(12))
