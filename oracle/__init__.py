@@ -103,10 +103,16 @@ class Oracle:
         lib.ada_oracle_prefill_append.restype = c_int
         lib.ada_oracle_threads.argtypes = []
         lib.ada_oracle_threads.restype = c_int
+        lib.ada_oracle_set_threads.argtypes = [c_int]
+        lib.ada_oracle_set_threads.restype = None
         self._lib = lib
 
     def threads(self) -> int:
         return int(self._lib.ada_oracle_threads())
+
+    def set_threads(self, n: int) -> None:
+        """Threads later calls may use (the results do not depend on it)."""
+        self._lib.ada_oracle_set_threads(int(n))
 
     def decode_bits(self, bits: np.ndarray, dtype: str) -> np.ndarray:
         """Decode an array of raw 16-bit patterns to float64, one by one."""

@@ -88,6 +88,16 @@ int ada_oracle_threads(void) {
 #endif
 }
 
+/* Sets the number of threads later calls may use (n >= 1); the results do
+ * not depend on it (each output row is computed by one thread). */
+void ada_oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /*
  * Single-token decode attention, grouped-query heads read in place.
  *
