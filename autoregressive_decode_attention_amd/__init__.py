@@ -21,7 +21,7 @@ The functions keep the C names without the ``ada_`` prefix:
   ``decode_combine(workspace, num_splits, out, n_kv_head)``: the two halves
 * ``prefill_append(k_new, v_new, k_cache, v_cache, start)`` and
   ``prefill_attn_gqa(q, k_cache, v_cache, start, ...)``: prompt prefill
-* ``decode_num_splits``, ``decode_workspace_bytes``, ``prefill_rows_per_workgroup``,
+* ``decode_num_splits``, ``decode_plan``, ``decode_workspace_bytes``, ``prefill_rows_per_workgroup``,
   ``device_num_cus``, ``status_string``, ``last_hip_error``, ``abi_version``.
 
 There is no fallback: if the library is missing, importing this package
@@ -51,7 +51,7 @@ STATUS = {
 
 EXPORTS = (
     "ada_abi_version", "ada_status_string", "ada_last_hip_error", "ada_device_num_cus",
-    "ada_kv_append", "ada_decode_num_splits", "ada_decode_workspace_bytes",
+    "ada_kv_append", "ada_decode_num_splits", "ada_decode_plan", "ada_decode_workspace_bytes",
     "ada_decode_attn_gqa", "ada_decode_attn_gqa_ex", "ada_decode_partial", "ada_decode_combine",
     "ada_decode_step", "ada_rope_kv_append", "ada_decode_step_rope", "ada_prefill_append",
     "ada_prefill_attn_gqa", "ada_prefill_rows_per_workgroup", "ada_step_graph_create", "ada_step_graph_launch", "ada_step_graph_destroy",
@@ -86,6 +86,7 @@ def _declare(lib):
         "ada_kv_append": ([c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                            c_int, c_void_p], c_int),
         "ada_decode_num_splits": ([c_int, c_int, c_int, c_int, c_int], c_int),
+        "ada_decode_plan": ([c_int] * 6 + [ctypes.POINTER(c_int), ctypes.POINTER(c_int)], c_int),
         "ada_decode_workspace_bytes": ([c_int, c_int, c_int, c_int, c_int], c_size_t),
         "ada_decode_attn_gqa": (decode_args, c_int),
         "ada_decode_attn_gqa_ex": (decode_args + [c_int], c_int),
@@ -168,6 +169,20 @@ def decode_num_splits(batch: int, n_head: int, n_kv_head: int, max_kv_len: int, 
     if num_cus is None:
         num_cus = _cus(torch.device("cuda", torch.cuda.current_device()))
     return int(_lib.ada_decode_num_splits(int(batch), int(n_head), int(n_kv_head), int(max_kv_len), int(num_cus)))
+
+
+def decode_plan(batch: int, n_head: int, n_kv_head: int, max_kv_len: int, num_splits: int = 0,
+                num_cus: int | None = None) -> tuple:
+    """(splits, chunk) of a decode call over ``max_kv_len`` slots, from the
+    library (``ada_decode_plan``): the heuristic on ``num_cus`` compute units
+    (default: the current device) when ``num_splits`` is 0, else the forced
+    count's near-equal ranges."""
+    if num_splits == 0 and num_cus is None:
+        num_cus = _cus(torch.device("cuda", torch.cuda.current_device()))
+    splits, chunk = ctypes.c_int(0), ctypes.c_int(0)
+    _check(_lib.ada_decode_plan(int(batch), int(n_head), int(n_kv_head), int(max_kv_len), int(num_splits),
+                                int(num_cus or 0), ctypes.byref(splits), ctypes.byref(chunk)), "ada_decode_plan")
+    return splits.value, chunk.value
 
 
 def prefill_rows_per_workgroup(batch: int, n_head: int, n_kv_head: int, q_len: int, num_cus: int | None = None) -> int:
@@ -286,11 +301,7 @@ def decode_attn_gqa_ex(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Te
     lens_t, mkl = _lengths(kv_len, max_kv_len, B, S, k_cache.device)
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
     plan_len = S if mkl <= 0 else min(mkl, S)  # the library reads max_kv_len <= 0 as the capacity
-    if num_splits > 0:
-        chunk = -(-plan_len // num_splits)
-        splits = -(-plan_len // chunk)
-    else:
-        splits = decode_num_splits(B, Hq, Hkv, plan_len)
+    splits, _ = decode_plan(B, Hq, Hkv, plan_len, num_splits)
     need = decode_workspace_bytes(B, Hq, Hkv, D, splits) if splits > 1 else 0
     ws = workspace if workspace is not None else _workspace(k_cache.device, need)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
@@ -334,11 +345,7 @@ def decode_partial(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor
     B, Hq, Hkv, S, D = _check_decode_inputs(q, k_cache, v_cache)
     lens_t, mkl = _lengths(kv_len, max_kv_len, B, S, k_cache.device)
     plan_len = S if mkl <= 0 else min(mkl, S)
-    if num_splits > 0:
-        chunk = -(-plan_len // num_splits)
-        splits = -(-plan_len // chunk)
-    else:
-        splits = decode_num_splits(B, Hq, Hkv, plan_len)
+    splits, _ = decode_plan(B, Hq, Hkv, plan_len, num_splits)
     if workspace is None:
         workspace = new_workspace(decode_workspace_bytes(B, Hq, Hkv, D, splits), k_cache.device)
     used = ctypes.c_int(0)
@@ -505,11 +512,7 @@ def _decode_step(q, k_new, v_new, cos, sin, k_cache, v_cache, pos, scale, out, m
             pos_t = _as_int32(host, B, k_cache.device)
             mp = max(0, min(S - 1, max(host))) if max_pos is None else int(max_pos)
     plan_len = min(mp + 1, S)
-    if num_splits > 0:
-        chunk = -(-plan_len // num_splits)
-        splits = -(-plan_len // chunk)
-    else:
-        splits = decode_num_splits(B, Hq, Hkv, plan_len)
+    splits, _ = decode_plan(B, Hq, Hkv, plan_len, num_splits)
     need = decode_workspace_bytes(B, Hq, Hkv, D, splits) if splits > 1 else 0
     ws = workspace if workspace is not None else _workspace(k_cache.device, need)
     ws_bytes = ws.numel() * ws.element_size() if ws is not None else 0
@@ -625,7 +628,7 @@ def decode_attn_gqa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
 __all__ = [
     "AdaError", "F16", "BF16", "HEAD_DIM", "MAX_SPLITS", "EXPORTS", "LIB_PATH", "load_library",
     "kv_append", "decode_attn_gqa", "decode_attn_gqa_ex", "decode_partial", "decode_combine", "decode_step", "decode_step_rope",
-    "rope_kv_append", "prefill_append", "prefill_attn_gqa", "decode_num_splits", "decode_workspace_bytes",
+    "rope_kv_append", "prefill_append", "prefill_attn_gqa", "decode_num_splits", "decode_plan", "decode_workspace_bytes",
     "new_workspace", "workspace_layout", "device_num_cus", "status_string", "last_hip_error",
     "abi_version", "StepGraph", "StepLayer", "step_graph", "prefill_rows_per_workgroup",
 ]

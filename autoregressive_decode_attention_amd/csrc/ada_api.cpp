@@ -162,6 +162,17 @@ int ada_decode_num_splits(int batch, int n_head, int n_kv_head, int max_kv_len, 
   return heuristic_plan(batch, n_head, n_kv_head, max_kv_len, num_cus).splits;
 }
 
+int ada_decode_plan(int batch, int n_head, int n_kv_head, int max_kv_len, int num_splits, int num_cus, int* splits,
+                    int* chunk) {
+  if (!splits || !chunk) return ADA_ERR_NULL;
+  if (num_splits < 0 || num_splits > ADA_MAX_SPLITS) return ADA_ERR_SPLITS;
+  const Plan p = num_splits > 0 ? forced_plan(max_kv_len, num_splits)
+                                : heuristic_plan(batch, n_head, n_kv_head, max_kv_len, num_cus);
+  *splits = p.splits;
+  *chunk = p.chunk;
+  return ADA_OK;
+}
+
 size_t ada_decode_workspace_bytes(int batch, int n_head, int n_kv_head, int head_dim, int num_splits) {
   if (num_splits < 1 || batch <= 0 || n_head <= 0 || n_kv_head <= 0 || head_dim <= 0) return 0;
   // sizes no call could use (and that would wrap size_t) report 0
@@ -175,6 +186,8 @@ int ada_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_c
   if (dtype != ADA_F16 && dtype != ADA_BF16) return ADA_ERR_DTYPE;
   if (batch < 0 || n_kv_head <= 0 || capacity <= 0) return ADA_ERR_SHAPE;
   if (head_dim != ada::kHeadDim) return ADA_ERR_HEAD_DIM;
+  // the launch indexes the rows' 16-byte chunks with 32-bit ints
+  if (sat_mul({batch, n_kv_head, ada::kHeadDim * 2 / 16}) > INT32_MAX - 255) return ADA_ERR_SHAPE;
   if (batch == 0) return ADA_OK;
   if (!k_new || !v_new || !k_cache || !v_cache || !pos) return ADA_ERR_NULL;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache))

@@ -98,6 +98,8 @@ int ada_device_num_cus(int device, int* num_cus);
  *                 [0, capacity) is skipped (nothing written), on the device.
  *
  * Values are copied bit for bit. k_new/v_new must not overlap the caches.
+ * ADA_ERR_SHAPE when batch * n_kv_head rows are too many to index with the
+ * launch's 32-bit thread indices (more than about 2^27).
  */
 int ada_kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                   const int32_t* pos, int batch, int n_kv_head, int capacity,
@@ -150,6 +152,20 @@ int ada_rope_kv_append(const void* q, void* q_out, const void* k_new, const void
  * (1 for non-positive inputs).
  */
 int ada_decode_num_splits(int batch, int n_head, int n_kv_head, int max_kv_len, int num_cus);
+
+/*
+ * The launch plan a decode call over max_kv_len slots uses: *splits key-range
+ * splits per (batch row, KV head) of *chunk slots each (the last may be
+ * shorter). num_splits == 0 gives the heuristic of ada_decode_num_splits for
+ * num_cus compute units; 1..ADA_MAX_SPLITS forces near-equal ranges of
+ * ceil(max_kv_len / num_splits) slots, as ada_decode_attn_gqa_ex does (fewer
+ * splits when the prefix is shorter; num_cus is then unused). Callers size
+ * workspaces with *splits (ada_decode_workspace_bytes). Pure host
+ * arithmetic: ADA_ERR_NULL for NULL outputs, ADA_ERR_SPLITS for num_splits
+ * outside [0, ADA_MAX_SPLITS], else ADA_OK (max_kv_len <= 0 gives 1 split).
+ */
+int ada_decode_plan(int batch, int n_head, int n_kv_head, int max_kv_len, int num_splits, int num_cus, int* splits,
+                    int* chunk);
 
 /*
  * Bytes of device workspace that holds num_splits (>= 1) per-split partial

@@ -122,6 +122,12 @@ int main() {
                              ptr(), nullptr);
     expect(known_status(s), true, "fuzz prefill");
     (void)ada_decode_num_splits(B, Hq, Hkv, n, pick());
+    {
+      int ps = 0, pc = 0;
+      s = ada_decode_plan(B, Hq, Hkv, n, splits, pick(), &ps, &pc);
+      expect(known_status(s), true, "fuzz plan");
+      if (s == ADA_OK) expect(ps >= 1 && ps <= ADA_MAX_SPLITS && pc >= 1, true, "fuzz plan range");
+    }
     (void)ada_decode_workspace_bytes(B, Hq, Hkv, D, splits);
     (void)ada_prefill_rows_per_workgroup(B, Hq, Hkv, n, pick());
     ada_step_layer layers[2];
@@ -140,6 +146,10 @@ int main() {
         for (int cus : {1, 80, 256, 304}) {
           const int sp = ada_decode_num_splits(B, 4 * Hkv, Hkv, n, cus);
           expect(sp >= 1 && sp <= ADA_MAX_SPLITS, true, "plan range");
+          int ps = 0, pc = 0;
+          expect(ada_decode_plan(B, 4 * Hkv, Hkv, n, 0, cus, &ps, &pc), ADA_OK, "plan call");
+          expect(ps == sp && static_cast<long>(ps) * pc >= n && static_cast<long>(ps - 1) * pc < n, true,
+                 "plan covers the prefix");
           expect(ada_decode_workspace_bytes(B, 4 * Hkv, Hkv, 128, sp) > 0, true, "plan workspace");
         }
   std::printf("abi driver: %d checks, %d failures\n", checks, failures);

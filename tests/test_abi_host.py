@@ -120,6 +120,9 @@ def test_append_validation(ada):
     assert f(P, P2, P3, P4, P5, 1, 8, 16, 64, 0, NUL) == -5
     assert f(MIS, P2, P3, P4, P5, 1, 8, 16, 128, 0, NUL) == -9
     assert f(NUL, NUL, NUL, NUL, NUL, 0, 8, 16, 128, 0, NUL) == 0
+    # rows * 16 chunks must be indexable by the launch's 32-bit thread ids
+    assert f(P, P2, P3, P4, P5, 65536, 2048, 16, 128, 0, NUL) == -2
+    assert f(P, P2, P3, P4, P5, 2**31 - 1, 2**31 - 1, 16, 128, 0, NUL) == -2
 
 
 def test_partial_and_combine_validation(ada):
@@ -337,3 +340,29 @@ def test_split_heuristic_properties(ada):
     assert ns(0, 8, 8, 100, 256) == 1
     assert ns(1, 8, 8, 0, 256) == 1
     assert ns(1, 8, 8, 100, 0) == 1
+
+
+def test_decode_plan_export(ada):
+    """ada_decode_plan: the heuristic's count (as ada_decode_num_splits) with
+    a chunk that covers the prefix in whole 64-slot tiles, or a forced count's
+    near-equal ranges; the binding sizes workspaces with it."""
+    plan = lambda B, Hq, Hkv, n, sp, cus=256: ada.decode_plan(B, Hq, Hkv, n, sp, cus)
+    for B, Hq, Hkv in ((1, 32, 8), (8, 32, 8), (1, 16, 16), (4, 32, 8), (3, 12, 3)):
+        for n in (1, 64, 65, 235, 400, 1258, 4096, 8192, 32768, 1 << 22):
+            s, c = plan(B, Hq, Hkv, n, 0)
+            assert s == ada.decode_num_splits(B, Hq, Hkv, n, 256)
+            assert s * c >= n > (s - 1) * c
+            if n > 256:
+                assert c % 64 == 0
+            for forced in (1, 2, 3, 7, 40, 256):
+                s, c = plan(B, Hq, Hkv, n, forced)
+                assert c == -(-n // forced) and s == -(-n // c) and s <= forced
+    assert plan(8, 32, 8, 32768, 0) == (8, 4096)
+    assert plan(1, 16, 16, 4096, 0) == (32, 128)
+    assert plan(1, 32, 8, 0, 5) == (1, 1)
+    f = ada._lib.ada_decode_plan
+    one = ctypes.c_int(0)
+    assert f(1, 32, 8, 100, 0, 256, None, ctypes.byref(one)) == -1
+    assert f(1, 32, 8, 100, 0, 256, ctypes.byref(one), None) == -1
+    assert f(1, 32, 8, 100, -1, 256, ctypes.byref(one), ctypes.byref(one)) == -8
+    assert f(1, 32, 8, 100, 257, 256, ctypes.byref(one), ctypes.byref(one)) == -8
