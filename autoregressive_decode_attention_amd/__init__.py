@@ -23,6 +23,7 @@ The functions keep the C names without the ``ada_`` prefix:
   ``prefill_attn_gqa(q, k_cache, v_cache, start, ...)``: prompt prefill
 * ``decode_num_splits``, ``decode_plan``, ``decode_workspace_bytes``, ``prefill_rows_per_workgroup``,
   ``device_num_cus``, ``status_string``, ``last_hip_error``, ``abi_version``.
+* ``hbm_read(src, sink, workgroups)``: measurement only, a plain streaming read
 
 There is no fallback: if the library is missing, importing this package
 raises ImportError.
@@ -55,6 +56,7 @@ EXPORTS = (
     "ada_decode_attn_gqa", "ada_decode_attn_gqa_ex", "ada_decode_partial", "ada_decode_combine",
     "ada_decode_step", "ada_rope_kv_append", "ada_decode_step_rope", "ada_prefill_append",
     "ada_prefill_attn_gqa", "ada_prefill_rows_per_workgroup", "ada_step_graph_create", "ada_step_graph_launch", "ada_step_graph_destroy",
+    "ada_hbm_read",
 )
 
 
@@ -106,6 +108,7 @@ def _declare(lib):
         "ada_step_graph_launch": ([c_void_p, c_void_p], c_int),
         "ada_prefill_rows_per_workgroup": ([c_int] * 5, c_int),
         "ada_step_graph_destroy": ([c_void_p], None),
+        "ada_hbm_read": ([c_void_p, c_size_t, c_void_p, c_int, c_void_p], c_int),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(lib, name)
@@ -612,6 +615,19 @@ def step_graph(layers, pos: torch.Tensor, max_pos: int, scale: float | None = No
     return StepGraph(handle.value, dev, tuple(keep))
 
 
+def hbm_read(src: torch.Tensor, sink: torch.Tensor, workgroups: int) -> None:
+    """Measurement: stream every byte of ``src`` (contiguous, 16-byte
+    aligned, size a multiple of 16) once on the current stream with the
+    decode kernel's loads; ``sink`` (uint32-sized, >= 4 * workgroups entries)
+    receives one xor per wavefront."""
+    _require(src.is_cuda and src.is_contiguous() and sink.is_cuda and sink.is_contiguous(),
+             "src and sink must be contiguous GPU tensors")
+    nbytes = src.numel() * src.element_size()
+    _require(sink.numel() * sink.element_size() >= 16 * workgroups, "sink needs 4 * workgroups uint32 entries")
+    _check(_lib.ada_hbm_read(_ptr(src), nbytes, _ptr(sink), int(workgroups), ctypes.c_void_p(_stream(src.device))),
+           "ada_hbm_read")
+
+
 def decode_attn_gqa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len,
                     scale: float | None = None, out: torch.Tensor | None = None,
                     max_kv_len: int | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
@@ -630,5 +646,5 @@ __all__ = [
     "kv_append", "decode_attn_gqa", "decode_attn_gqa_ex", "decode_partial", "decode_combine", "decode_step", "decode_step_rope",
     "rope_kv_append", "prefill_append", "prefill_attn_gqa", "decode_num_splits", "decode_plan", "decode_workspace_bytes",
     "new_workspace", "workspace_layout", "device_num_cus", "status_string", "last_hip_error",
-    "abi_version", "StepGraph", "StepLayer", "step_graph", "prefill_rows_per_workgroup",
+    "abi_version", "StepGraph", "StepLayer", "step_graph", "prefill_rows_per_workgroup", "hbm_read",
 ]

@@ -639,3 +639,16 @@ void ada_step_graph_destroy(ada_step_graph* graph) {
 }
 
 }  // extern "C"
+
+extern "C" {
+
+int ada_hbm_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, void* stream) {
+  if (workgroups <= 0 || workgroups > (1 << 20) || bytes % 16 != 0) return ADA_ERR_SHAPE;
+  if (bytes == 0) return ADA_OK;
+  if (!src || !sink) return ADA_ERR_NULL;
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u) != 0) return ADA_ERR_ALIGN;
+  hipError_t e = ada::launch_hbm_read(src, bytes, sink, workgroups, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ADA_OK : hip_fail(e);
+}
+
+}  // extern "C"

@@ -101,4 +101,8 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache,
 
 hipError_t launch_advance_positions(int32_t* pos, int batch, int delta, hipStream_t stream);
 
+// Streaming read of `bytes` (a multiple of 16) from src by `workgroups`
+// 256-thread workgroups; one 32-bit xor per wavefront to sink.
+hipError_t launch_hbm_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t stream);
+
 }  // namespace ada

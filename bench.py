@@ -1,28 +1,32 @@
 """Benchmark of the single-token decode-attention hot path on one MI355X.
 
-A step is one pass of the whole hot path over the one-token MHA decode sweep
-of Cuda-Compute-OSS #343 ("Current limitation"): batch 1, 16 query heads = 16
-KV heads, head_dim 128, fp16, capacity 8192; for each kv_len in
-(1024, 4096, 8192): append the new K/V rows at slot kv_len - 1, then decode
-over kv_len slots. Each kv_len has its own cache, and steps rotate over 5 sets
-of caches (960 MiB) so that no call finds its K/V in the 256 MB Infinity Cache:
-the inputs sit in HBM when the timed region starts.
+A step is one pass of the whole hot path over the long-context workload
+(batch 8, 32 query heads sharing 8 KV heads, head_dim 128, bf16, kv_len 32768
+= the full capacity, 1 % of key rows scaled x8): one ada_decode_step call that
+appends the new key and value rows at the last slot (the append is folded
+into the partial kernel), picks the split plan on the host, streams all
+32768 slots of every (batch row, KV head) in the split-KV partial kernel and
+merges the splits in the combine kernel. A call reads 1.07 GB, four times
+the 256 MB Infinity Cache, so every step streams from HBM. The grouped-query
+decode this workload stresses is the one the pages measure at a K width of
+32768 (fish-speech PR #1337, "Isolated SDPA-kernel benchmark").
 
-The timed region replays one HIP graph per step (the step's 9 kernels:
-3 x append, partial, combine); eager launches from Python are reported
-beside it. Printed: one JSON line with the metric (achieved algorithmic GB/s
-over the timed steps), the roofline of the dominant kernel (the split-KV
-partial: algorithmic bytes / its average duration over back-to-back launches
-bracketed by HIP events, with the host queued ahead so that launch cost does
-not count, against 8 TB/s), the fp64 CPU oracle timed on a bounded sample of
-the same step, and, under "also", the per-kv_len figures, the
-long-context workload (batch 8, 32/8 heads, bf16, kv_len 32768, 1.07 GB per
-call), the 36-layer S2-Pro-shaped run, the MiniCPM-shaped streaming
-workload (lockstep positions and ragged batches), the full-capacity against
-active-prefix comparison, the decode step with rotary embedding, and the
-causal prompt prefill.
+Printed: one JSON line with the metric (achieved algorithmic GB/s of the
+timed steps), the roofline of the dominant kernel (the partial kernel:
+algorithmic bytes / its average duration over back-to-back launches bracketed
+by HIP events on the launching stream, with the host queued ahead so that
+launch cost does not count, against 8 TB/s; traffic from the committed
+rocprofv3 counter summary), the fp64 CPU oracle timed on the host cores,
+and, under "also": every graded point against its 70 %-of-peak bar (the MHA
+sweep at kv_len 4096 and 8192, the MiniCPM shape at positions 4095 and 8191
+and its ragged draws, this workload), a streaming-read floor at the same
+sizes, the 36-layer S2-Pro-shaped run, the MiniCPM lockstep sweep, the
+full-capacity against active-prefix comparison, the decode step with rotary
+embedding, one GPU's share under an 8-way split, and the causal prompt
+prefill.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       [--long-context-only] [--only SECTIONS] [--prefill-only]
 """
 from __future__ import annotations
 
@@ -52,7 +56,11 @@ CALIB_BYTES = 256 * 2**20  # calibration copy for the counter runs
 SPIN_CYCLES = 100_000_000  # GPU-side spin (about 40 ms) that lets the host run ahead
 SWEEP = (1024, 4096, 8192)
 KERNEL_SOURCE = ROOT / "autoregressive_decode_attention_amd" / "csrc" / "ada_kernels.hip"
-PMC_SUMMARY = ROOT / "profiles" / "decode_kernel_mha_sweep_pmc.md"
+PMC_SUMMARY = ROOT / "profiles" / "decode_kernel_long_context_pmc.md"
+ROOFLINE_MIN_LAUNCHES = 100
+# Sections of "also" (bench.py --only picks some).
+SECTIONS = ("mha_sweep", "minicpm_stream", "read_floor", "graded", "shards", "s2pro_run",
+            "full_capacity_vs_active_prefix", "minicpm_sweep", "rope_step", "prefill")
 
 
 # ---------------------------------------------------------------------------
@@ -80,24 +88,83 @@ def kernel_source_hash() -> str:
 
 
 def pmc_traffic() -> float | None:
-    """HBM bytes of one step's partial-kernel launches from the committed
-    rocprofv3 counter summary, or None when there is none or the kernel source
-    changed since the counters were taken."""
+    """HBM bytes (reads + writes) of one partial-kernel launch of the
+    long-context workload from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since the counters
+    were taken."""
     if not PMC_SUMMARY.exists():
         return None
     text = PMC_SUMMARY.read_text()
     m = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
-    t = re.search(r"traffic_bytes_per_step_decode:\s*([0-9.eE+]+)", text)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not m or not t or m.group(1) != kernel_source_hash():
         return None
     return float(t.group(1))
+
+
+def bar_us(nbytes: int, frac: float = 0.7) -> float:
+    """Duration at ``frac`` of the 8 TB/s peak for ``nbytes`` bytes."""
+    return nbytes / (frac * PEAK_HBM_GBS * 1e3)
+
+
+def device_timed(fn, iters: int) -> float:
+    """Average device time (us) of ``iters`` back-to-back calls of fn(i),
+    bracketed by HIP events on the current stream; a GPU-side spin queued
+    first lets the host enqueue every call before the first runs, so host
+    launch cost does not show up as gaps."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(SPIN_CYCLES)
+    a.record()
+    for i in range(iters):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / iters
+
+
+class LongContext:
+    """The long-context workload: batch 8, 32/8 heads, head_dim 128, bf16,
+    kv_len 32768 = capacity, 1 % of key rows x8 (the outlier rows stress the
+    softmax range). One step = ada_decode_step appending at the last slot and
+    attending over all 32768 slots (append folded into the partial kernel,
+    host split plan, partial kernel, combine kernel)."""
+
+    def __init__(self, ada, device):
+        self.ada = ada
+        wl = W.WORKLOADS["long_context"]
+        self.shape = shp = wl.shape
+        B, Hq, Hkv, D, S = shp.batch, shp.n_head, shp.n_kv_head, shp.head_dim, shp.capacity
+        x = W.decode_inputs(shp, [S] * B, W.seed_for(4), device=device, tail="random",
+                            outlier_p=wl.outlier_p, outlier_scale=wl.outlier_scale)
+        self.q, self.k_cache, self.v_cache = x["q"], x["k_cache"], x["v_cache"]
+        self.k_new, self.v_new = W.append_inputs(B, Hkv, D, shp.dtype, W.seed_for(4, 1), device=device)
+        self.pos = S - 1
+        self.splits, self.chunk = ada.decode_plan(B, Hq, Hkv, S)
+        self.ws = ada.new_workspace(ada.decode_workspace_bytes(B, Hq, Hkv, D, max(2, self.splits)), device)
+        self.out = torch.empty_like(self.q)
+        self.scale = 1.0 / math.sqrt(D)
+        self.partial_bytes = kv_bytes(Hkv, D, B * S) + B * Hq * D * 2  # K, V and q read
+        self.call_bytes = decode_bytes(B, Hq, Hkv, D, [S] * B)
+        self.step_bytes = self.call_bytes + append_bytes(B, Hkv, D)
+
+    def step(self, i: int = 0):
+        self.ada.decode_step(self.q, self.k_new, self.v_new, self.k_cache, self.v_cache, self.pos,
+                             scale=self.scale, out=self.out, workspace=self.ws)
+
+    def partial(self, i: int = 0):
+        self.ada.decode_partial(self.q, self.k_cache, self.v_cache, None, scale=self.scale,
+                                max_kv_len=self.shape.capacity, workspace=self.ws)
 
 
 # ---------------------------------------------------------------------------
 
 
 class Sweep:
-    """The one-token MHA decode sweep with rotating cold caches."""
+    """The one-token MHA decode sweep of Cuda-Compute-OSS #343 ("Current
+    limitation"): batch 1, 16 query heads = 16 KV heads, head_dim 128, fp16,
+    kv_len 1024 / 4096 / 8192, each with its own caches, rotated over enough
+    sets (960 MiB) that no call finds its K/V in the 256 MB Infinity Cache."""
 
     def __init__(self, ada, device, sets: int | None = None):
         self.ada = ada
@@ -115,52 +182,12 @@ class Sweep:
                 row.append((x["k_cache"], x["v_cache"]))
             self.caches.append(row)
         self.q = [W.randn16((B, Hq, D), shp.dtype, W.seed_for(1, 7000 + j), device=device) for j in range(3)]
-        self.k_new, self.v_new = W.append_inputs(B, Hkv, D, shp.dtype, W.seed_for(1, 9000), device=device)
-        self.pos = [torch.full((B,), n - 1, dtype=torch.int32, device=device) for n in SWEEP]
-        self.lens = [torch.full((B,), n, dtype=torch.int32, device=device) for n in SWEEP]
         self.out = [torch.empty((B, Hq, D), dtype=W.TORCH_DTYPES[shp.dtype], device=device) for _ in SWEEP]
         self.scale = 1.0 / math.sqrt(D)
         self.decode_bytes = [decode_bytes(B, Hq, Hkv, D, [n]) for n in SWEEP]
-        self.step_bytes = sum(self.decode_bytes) + 3 * append_bytes(B, Hkv, D)
-        self.i = 0
         ws_need = max(ada.decode_workspace_bytes(B, Hq, Hkv, D, max(2, ada.decode_num_splits(B, Hq, Hkv, n)))
                       for n in SWEEP)
         self.ws = ada.new_workspace(ws_need, device)
-
-    def step(self, set_index: int | None = None):
-        """One decode step at each kv_len -- append the new row at slot kv_len - 1
-        and attend over kv_len slots, as one ada_decode_step call (partial
-        kernel with the append folded in, then the combine kernel) -- on the
-        next cache set (or ``set_index``). The position is a host int (batch
-        1), so the kernels read no length from the device."""
-        ada = self.ada
-        row = self.caches[(self.i if set_index is None else set_index) % self.sets]
-        self.i += 1
-        for j, n in enumerate(SWEEP):
-            k, v = row[j]
-            ada.decode_step(self.q[j], self.k_new, self.v_new, k, v, n - 1, scale=self.scale, out=self.out[j],
-                            workspace=self.ws)
-
-    def capture(self):
-        """One HIP graph per cache set holding a whole step (6 kernels)."""
-        self.graphs = []
-        stream = torch.cuda.Stream()
-        stream.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(stream):
-            for s in range(self.sets):  # warm the binding's caches outside capture
-                self.step(s)
-        torch.cuda.current_stream().wait_stream(stream)
-        torch.cuda.synchronize()
-        for s in range(self.sets):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                self.step(s)
-            self.graphs.append(g)
-        torch.cuda.synchronize()
-
-    def replay(self):
-        self.graphs[self.i % self.sets].replay()
-        self.i += 1
 
     def time_partials(self, iters: int) -> list:
         """Average duration of the partial kernel per kv_len: ``iters`` launches
@@ -207,49 +234,6 @@ class Sweep:
             torch.cuda.synchronize()
             res.append(a.elapsed_time(b) * 1e3 / iters)
         return res
-
-
-def time_long_context(ada, device, iters: int = 20) -> dict:
-    """The long-context workload (1.07 GB per call, 4x the Infinity Cache, so
-    every call streams from HBM): average partial-kernel and whole-call
-    durations over back-to-back launches bracketed by HIP events."""
-    wl = W.WORKLOADS["long_context"]
-    shp = wl.shape
-    x = W.decode_inputs(shp, [shp.capacity] * shp.batch, W.seed_for(4), device=device, tail="random",
-                        outlier_p=wl.outlier_p, outlier_scale=wl.outlier_scale)
-    B, Hq, Hkv, D = shp.batch, shp.n_head, shp.n_kv_head, shp.head_dim
-    splits = ada.decode_num_splits(B, Hq, Hkv, shp.capacity)
-    ws = ada.new_workspace(ada.decode_workspace_bytes(B, Hq, Hkv, D, max(2, splits)), device)
-    out = torch.empty_like(x["q"])
-    scale = 1.0 / math.sqrt(D)
-
-    def partial():
-        return ada.decode_partial(x["q"], x["k_cache"], x["v_cache"], None, scale=scale,
-                                  max_kv_len=shp.capacity, workspace=ws)[1]
-
-    def timed(fn):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        torch.cuda._sleep(SPIN_CYCLES)
-        a.record()
-        for _ in range(iters):
-            fn()
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) * 1e3 / iters
-
-    for _ in range(3):
-        ada.decode_combine(ws, partial(), out, Hkv)
-    part = timed(partial)
-    whole = timed(lambda: ada.decode_combine(ws, partial(), out, Hkv))
-    nbytes = decode_bytes(B, Hq, Hkv, D, [shp.capacity] * B)
-    del x
-    return {"workload": "long_context: batch 8, 32/8 heads, head_dim 128, bf16, kv_len 32768, 1% keys x8",
-            "bytes_per_call": nbytes, "splits": splits,
-            "partial_us": round(part, 2), "partial_GBs": round(nbytes / part / 1e3, 1),
-            "partial_frac_of_peak": round(nbytes / part / 1e3 / PEAK_HBM_GBS, 4),
-            "call_us": round(whole, 2), "call_GBs": round(nbytes / whole / 1e3, 1),
-            "call_frac_of_peak": round(nbytes / whole / 1e3 / PEAK_HBM_GBS, 4)}
 
 
 def time_shards(ada, device, iters: int = 20) -> dict:
@@ -551,7 +535,7 @@ def time_minicpm_stream(ada, device, iters: int = 50, draws: int = 64) -> dict:
         us = timed(lambda i, p=p: ada.decode_step(xs[i % R]["q"], k_new, v_new, xs[i % R]["k_cache"],
                                                   xs[i % R]["v_cache"], p, scale=scale, out=out, workspace=ws))
         nb = decode_bytes(B, Hq, Hkv, D, [p + 1] * B)
-        res[f"lockstep_p{p}"] = {"us": round(us, 2), "GBs": round(nb / us / 1e3, 1),
+        res[f"lockstep_p{p}"] = {"bytes": nb, "us": round(us, 2), "GBs": round(nb / us / 1e3, 1),
                                  "frac_of_peak": round(nb / us / 1e3 / PEAK_HBM_GBS, 4)}
         pt = torch.full((B,), p, dtype=torch.int32, device=device)
         us = timed(lambda i, pt=pt: ada.decode_step(xs[i % R]["q"], k_new, v_new, xs[i % R]["k_cache"],
@@ -569,10 +553,13 @@ def time_minicpm_stream(ada, device, iters: int = 50, draws: int = 64) -> dict:
     tot_b = sum(r[2] for r in rows)
     tot_us = sum(r[1] for r in rows)
     big = [r for r in rows if sum(r[0]) / B >= 4096]
+    big_b, big_us = sum(r[2] for r in big), sum(r[1] for r in big)
     res["ragged"] = {"draws": draws, "mean_us": round(tot_us / draws, 2), "GBs": round(tot_b / tot_us / 1e3, 1),
                      "frac_of_peak": round(tot_b / tot_us / 1e3 / PEAK_HBM_GBS, 4),
                      "draws_mean_len_ge_4096": len(big),
-                     "GBs_mean_len_ge_4096": round(sum(r[2] for r in big) / max(1e-9, sum(r[1] for r in big)) / 1e3, 1)}
+                     "bytes_mean_len_ge_4096": big_b // max(1, len(big)),
+                     "us_mean_len_ge_4096": round(big_us / max(1, len(big)), 2),
+                     "GBs_mean_len_ge_4096": round(big_b / max(1e-9, big_us) / 1e3, 1)}
     del xs
     return res
 
@@ -616,33 +603,133 @@ def time_prefill(ada, device, iters: int = 30) -> dict:
     return res
 
 
-def cpu_baseline(seconds: float) -> dict:
-    """The fp64 oracle on the same step (three decode calls of the sweep), run
-    until ``seconds`` of CPU time have passed (at least one step)."""
+READ_FLOOR_POOL = 2 * 2**30  # bytes of the buffer the read probe rotates over
+
+
+def time_read_floor(ada, device, sizes, iters: int = 20) -> list:
+    """The streaming-read floor at each size (bytes): ada_hbm_read, the
+    decode kernel's loads with no arithmetic, over a 2 GiB pool (calls rotate
+    over disjoint regions, so sizes below the 256 MB Infinity Cache still
+    come from HBM), at several workgroup counts; the best is reported."""
+    pool = torch.empty(READ_FLOOR_POOL, dtype=torch.uint8, device=device)
+    pool.fill_(1)
+    sink = torch.empty(4 * 8192, dtype=torch.int32, device=device)
+    rows = []
+    for nbytes in sizes:
+        nbytes = (int(nbytes) + 15) // 16 * 16
+        regions = max(1, READ_FLOOR_POOL // nbytes)
+        views = [pool[r * nbytes:(r + 1) * nbytes] for r in range(min(regions, 64))]
+        best = None
+        for wgs in (256, 512, 1024, 2048, 4096, 8192):
+            ada.hbm_read(views[0], sink, wgs)
+            us = device_timed(lambda i, wgs=wgs: ada.hbm_read(views[i % len(views)], sink, wgs), iters)
+            if best is None or us < best[1]:
+                best = (wgs, us)
+        rows.append({"bytes": nbytes, "best_workgroups": best[0], "us": round(best[1], 2),
+                     "GBs": round(nbytes / best[1] / 1e3, 1),
+                     "frac_of_peak": round(nbytes / best[1] / 1e3 / PEAK_HBM_GBS, 4),
+                     "regions_rotated": len(views)})
+    del pool, sink
+    return rows
+
+
+def graded_points(lc_call_us: float, lc_bytes: int, per_kv: list, minicpm: dict, floor: list) -> list:
+    """Every point the 70 %-of-peak target applies to (kv_len >= 4096): bytes
+    per call, the bar (duration at 70 % of 8 TB/s), the measured whole-call
+    duration and its fraction of peak, and the streaming-read floor of the
+    same bytes."""
+    fl = {r["bytes"]: r for r in floor}
+
+    def row(name, nbytes, us):
+        f = fl.get((nbytes + 15) // 16 * 16)
+        return {"point": name, "bytes": nbytes, "bar_us": round(bar_us(nbytes), 2), "us": round(us, 2),
+                "frac_of_peak": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4), "meets_bar": us <= bar_us(nbytes),
+                "read_floor_us": f["us"] if f else None}
+
+    out = []
+    for r in per_kv:
+        if r["kv_len"] >= 4096:
+            out.append(row(f"mha_sweep kv_len {r['kv_len']} (decode call)", r["bytes"], r["call_us"]))
+    for p in (4095, 8191):
+        m = minicpm[f"lockstep_p{p}"]
+        out.append(row(f"minicpm_stream lockstep position {p} (decode step)", m["bytes"], m["us"]))
+    rg = minicpm["ragged"]
+    if rg["draws_mean_len_ge_4096"]:
+        out.append(row(f"minicpm_stream ragged, {rg['draws_mean_len_ge_4096']} draws with mean kv_len >= 4096 "
+                       "(decode call, mean)", rg["bytes_mean_len_ge_4096"], rg["us_mean_len_ge_4096"]))
+    out.append(row("long_context (decode step)", lc_bytes, lc_call_us))
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline() -> dict:
+    """The fp64 oracle (oracle/ada_oracle.c, OpenMP over (batch row, query
+    head)) on the host cores, on the same seeded inputs as the GPU: the
+    headline figure is one whole long-context call at nproc threads; beside
+    it, every workload at 1 thread and at nproc threads (the long-context
+    call at 1 thread on one of its 8 batch rows). GB/s counts the same
+    algorithmic bytes as the GPU figures."""
     import oracle
 
     ora = oracle.load()
-    shp = W.WORKLOADS["mha_sweep"].shape
-    B, Hq, Hkv, D = shp.batch, shp.n_head, shp.n_kv_head, shp.head_dim
-    inputs = []
-    for j, n in enumerate(SWEEP):
-        x = W.decode_inputs(W.DecodeShape(B, Hq, Hkv, D, n, shp.dtype), [n], W.seed_for(1, j), tail="random")
-        inputs.append((x, n))
-    scale = 1.0 / math.sqrt(D)
-    steps = 0
-    t0 = time.perf_counter()
-    while True:
-        for x, n in inputs:
-            ora.decode(x["q"], x["k_cache"], x["v_cache"], [n], scale)
-        steps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    nbytes = steps * sum(decode_bytes(B, Hq, Hkv, D, [n]) for n in SWEEP)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": ora.threads(), "kind": "oracle",
-            "sample": f"{steps} steps of the MHA sweep decode calls (kv_len 1024/4096/8192, batch 1, 16 heads, "
-                      f"fp16) in {dt:.1f} s; cache appends not included",
-            "ms_per_step": round(dt / steps * 1e3, 2)}
+    nproc = os.cpu_count() or 1
+    scale = 1.0 / math.sqrt(128)
+
+    def case(name, shp, lens, seed, outliers=None):
+        x = W.decode_inputs(W.DecodeShape(len(lens), shp.n_head, shp.n_kv_head, shp.head_dim, shp.capacity,
+                                          shp.dtype), lens, seed, tail="random",
+                            **({} if outliers is None else {"outlier_p": outliers[0], "outlier_scale": outliers[1]}))
+        return name, x, lens, decode_bytes(len(lens), shp.n_head, shp.n_kv_head, shp.head_dim, lens)
+
+    def run(x, lens, threads):
+        ora.set_threads(threads)
+        t = time.perf_counter()
+        ora.decode(x["q"], x["k_cache"], x["v_cache"], lens, scale)
+        return time.perf_counter() - t
+
+    wl = W.WORKLOADS
+    lc = wl["long_context"]
+    cases = [case("tiny (kv_len 400)", wl["tiny"].shape, [400], W.seed_for(0))]
+    for n in SWEEP:
+        s2 = wl["mha_sweep"].shape
+        cases.append(case(f"mha_sweep kv_len {n}", W.DecodeShape(1, s2.n_head, s2.n_kv_head, 128, n, s2.dtype), [n],
+                          W.seed_for(1, n)))
+    for n in (235, 1258):
+        cases.append(case(f"s2pro_run one layer-call, kv_len {n}", wl["s2pro_run"].shape, [n], W.seed_for(2, n)))
+    mc = wl["minicpm_stream"].shape
+    cases.append(case("minicpm_stream lockstep position 8191", mc, [8192] * 4, W.seed_for(3, 8191)))
+    cases.append(case("minicpm_stream ragged draw", mc, W.ragged_lengths(4, 1, mc.capacity, W.seed_for(3, 72_000)),
+                      W.seed_for(3, 72_000)))
+    lc_shape = lc.shape
+    one_row = case("long_context, batch row 0 of 8", W.DecodeShape(1, lc_shape.n_head, lc_shape.n_kv_head, 128,
+                                                                    lc_shape.capacity, lc_shape.dtype),
+                   [lc_shape.capacity], W.seed_for(4), (lc.outlier_p, lc.outlier_scale))
+    table = []
+    for name, x, lens, nb in cases + [one_row]:
+        t1 = run(x, lens, 1)
+        tn = run(x, lens, nproc)
+        table.append({"workload": name, "bytes": nb, "ms_1_thread": round(t1 * 1e3, 2),
+                      "GBs_1_thread": round(nb / t1 / 1e9, 4), f"ms_{nproc}_threads": round(tn * 1e3, 2),
+                      f"GBs_{nproc}_threads": round(nb / tn / 1e9, 4)})
+    del cases, one_row
+    name, x, lens, nb = case("long_context", lc_shape, [lc_shape.capacity] * lc_shape.batch, W.seed_for(4),
+                             (lc.outlier_p, lc.outlier_scale))
+    t = run(x, lens, nproc)
+    ora.set_threads(nproc)
+    return {"value": round(nb / t / 1e9, 4), "unit": "GB/s", "cores": nproc, "kind": "oracle",
+            "sample": f"one whole long-context decode call (batch 8, 32/8 heads, kv_len 32768, bf16, "
+                      f"{nb} algorithmic bytes) in {t:.2f} s at {nproc} threads; the cache append not included",
+            "ms_per_call": round(t * 1e3, 1), "cpu_model": cpu_model(), "nproc": nproc,
+            "per_workload": table}
 
 
 def main(argv=None):
@@ -651,8 +738,12 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-long-context", action="store_true")
+    ap.add_argument("--long-context-only", action="store_true",
+                    help="the contract line of the long-context workload only (no other workloads, no step-graph "
+                         "replays): for counter passes")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated sections of 'also' to run (default: all): " + ", ".join(SECTIONS) +
+                         "; graded and read_floor need mha_sweep and minicpm_stream")
     ap.add_argument("--prefill-only", action="store_true",
                     help="time only the prompt prefill cases and print them (for profiling runs); "
                          "no contract line")
@@ -665,10 +756,10 @@ def main(argv=None):
     import autoregressive_decode_attention_amd as ada
 
     device = torch.device("cuda", 0)
+    torch.cuda.set_device(device)
     if args.prefill_only:
         print(json.dumps({"prefill": time_prefill(ada, device)}), flush=True)
         return 0
-    torch.cuda.set_device(device)
     # A plain copy of known size (256 MiB read, 256 MiB written): the reference
     # that scales the FETCH_SIZE / WRITE_SIZE counters of the profiled runs.
     calib_src = torch.empty(CALIB_BYTES // 2, dtype=torch.float16, device=device).fill_(1.0)
@@ -677,80 +768,97 @@ def main(argv=None):
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
-    sweep = Sweep(ada, device)
-    launch = "hip_graph"
-    try:
-        sweep.capture()
-    except Exception as exc:  # graph capture unavailable: time eager launches instead
-        launch = f"eager ({type(exc).__name__})"
-        sweep.graphs = None
-    run_step = sweep.replay if sweep.graphs else sweep.step
+    lc = LongContext(ada, device)
     for _ in range(args.warmup):
-        run_step()
+        lc.step()
     torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    ev0.record()
     for _ in range(args.steps):
-        run_step()
+        lc.step()
+    ev1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    value = sweep.step_bytes / (ms_per_step * 1e-3) / 1e9
+    value = lc.step_bytes / (ms_per_step * 1e-3) / 1e9
+    step_dev_us = ev0.elapsed_time(ev1) * 1e3 / args.steps
 
-    # Eager steps (every kernel launched from Python through the C ABI).
-    torch.cuda.synchronize()
-    e0 = time.perf_counter()
-    for _ in range(args.steps):
-        sweep.step()
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - e0) * 1e3 / args.steps
-
-    part_us = sweep.time_partials(args.steps)
-    call_us = sweep.time_calls(args.steps)
-    hot_us = sweep.time_calls(args.steps, resident=True)
-    per_kv = []
-    for j, n in enumerate(SWEEP):
-        nb = sweep.decode_bytes[j]
-        per_kv.append({"kv_len": n, "bytes": nb, "splits": ada.decode_num_splits(1, 16, 16, n),
-                       "partial_us": round(part_us[j], 2), "partial_GBs": round(nb / part_us[j] / 1e3, 1),
-                       "call_us": round(call_us[j], 2), "call_GBs": round(nb / call_us[j] / 1e3, 1),
-                       "call_frac_of_peak": round(nb / call_us[j] / 1e3 / PEAK_HBM_GBS, 4),
-                       "cache_resident_call_us": round(hot_us[j], 2),
-                       "cache_resident_call_GBs": round(nb / hot_us[j] / 1e3, 1)})
-    achieved = sum(sweep.decode_bytes) / sum(part_us) / 1e3
+    # Roofline of the dominant kernel: the partial kernel of the same call,
+    # launched back to back; and the whole step the same way.
+    n_roof = max(args.steps, ROOFLINE_MIN_LAUNCHES)
+    lc.partial()
+    part_us = device_timed(lc.partial, n_roof)
+    call_us = device_timed(lc.step, n_roof)
+    achieved = lc.partial_bytes / part_us / 1e3
     traffic = pmc_traffic()
-
-    also = {"per_kv_len": per_kv, "eager_ms_per_step": round(eager_ms, 4),
-            "eager_GBs": round(sweep.step_bytes / (eager_ms * 1e-3) / 1e9, 1)}
-    if not args.no_long_context:
-        also["long_context"] = time_long_context(ada, device)
-        also["shards"] = time_shards(ada, device)
-        also["s2pro_run"] = time_s2pro_run(ada, device)
-        also["full_capacity_vs_active_prefix"] = time_full_vs_active(ada, device)
-        also["minicpm_stream"] = time_minicpm_stream(ada, device)
-        also["minicpm_sweep"] = time_minicpm_sweep(ada, device)
-        also["rope_step"] = time_rope_step(ada, device)
-        also["prefill"] = time_prefill(ada, device)
+    headline = {"step_us_events_timed_region": round(step_dev_us, 2),
+                "step_us_back_to_back": round(call_us, 2), "step_launches_back_to_back": n_roof,
+                "step_GBs_back_to_back": round(lc.step_bytes / call_us / 1e3, 1),
+                "step_frac_of_peak_back_to_back": round(lc.step_bytes / call_us / 1e3 / PEAK_HBM_GBS, 4),
+                "bar_us_70pct": round(bar_us(lc.step_bytes), 2), "splits": lc.splits, "chunk": lc.chunk}
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "fp16", "data": "synthetic",
-        "config": {"workload": "mha_sweep: one-token decode, batch 1, 16 heads = 16 KV heads, head_dim 128, fp16, "
-                               "kv_len 1024/4096/8192 (append + decode each), capacity 8192, "
-                               f"cold caches rotated over {sweep.sets} sets",
-                   "step_bytes": sweep.step_bytes, "kernels_per_step": 6, "launch": launch},
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "long_context: one-token GQA decode step, batch 8, 32 query heads / 8 KV heads, "
+                               "head_dim 128, bf16, kv_len 32768 = capacity, 1% of key rows x8 (append at slot "
+                               "32767, attend over 32768 slots)",
+                   "step_bytes": lc.step_bytes, "kernels_per_step": 1 if lc.splits == 1 else 2,
+                   "launch": "eager (ada_decode_step per step)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "traffic_basis": "HBM bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated) of the three partial "
-                                      "launches of one step; algorithmic bytes of the same launches: "
-                                      f"{sum(sweep.decode_bytes)}",
-                     "kernel": "partial_kernel (split-KV partial of the decode; the combine kernel follows it)",
-                     "bytes_per_launch": sweep.decode_bytes,
-                     "us_per_launch": [round(u, 2) for u in part_us]},
-        "also": also,
+                     "traffic_basis": "HBM bytes (FETCH_SIZE + WRITE_SIZE, copy-calibrated) of one partial launch of "
+                                      f"this workload; algorithmic bytes of that launch: {lc.partial_bytes}",
+                     "kernel": "partial_kernel<bf16, G=4> (split-KV partial; the combine kernel follows it)",
+                     "bytes_per_launch": lc.partial_bytes, "us_per_launch": round(part_us, 2),
+                     "launches_timed": n_roof},
+        "also": {"headline": headline},
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    wanted = set(SECTIONS) if args.only is None else {x for x in args.only.split(",") if x}
+    unknown = wanted - set(SECTIONS)
+    if unknown:
+        print(f"unknown sections: {sorted(unknown)}", file=sys.stderr)
+        return 2
+    if args.long_context_only:
+        wanted = set()
+    also = line["also"]
+    if "mha_sweep" in wanted:
+        sweep = Sweep(ada, device)
+        part_mha = sweep.time_partials(max(args.steps, ROOFLINE_MIN_LAUNCHES))
+        call_mha = sweep.time_calls(max(args.steps, ROOFLINE_MIN_LAUNCHES))
+        hot_mha = sweep.time_calls(max(args.steps, ROOFLINE_MIN_LAUNCHES), resident=True)
+        per_kv = []
+        for j, n in enumerate(SWEEP):
+            nb = sweep.decode_bytes[j]
+            per_kv.append({"kv_len": n, "bytes": nb, "splits": ada.decode_num_splits(1, 16, 16, n),
+                           "partial_us": round(part_mha[j], 2), "partial_GBs": round(nb / part_mha[j] / 1e3, 1),
+                           "call_us": round(call_mha[j], 2), "call_GBs": round(nb / call_mha[j] / 1e3, 1),
+                           "call_frac_of_peak": round(nb / call_mha[j] / 1e3 / PEAK_HBM_GBS, 4),
+                           "cache_resident_call_us": round(hot_mha[j], 2),
+                           "cache_resident_call_GBs": round(nb / hot_mha[j] / 1e3, 1)})
+        del sweep
+        also["mha_sweep"] = per_kv
+    if "minicpm_stream" in wanted:
+        also["minicpm_stream"] = time_minicpm_stream(ada, device)
+    lc_sizes = (lc.partial_bytes, lc.step_bytes)
+    del lc
+    if {"read_floor", "graded"} & wanted and {"mha_sweep", "minicpm_stream"} <= wanted:
+        mc = also["minicpm_stream"]
+        sizes = sorted({r["bytes"] for r in also["mha_sweep"] if r["kv_len"] >= 4096} |
+                       {mc[f"lockstep_p{p}"]["bytes"] for p in (4095, 8191)} |
+                       {mc["ragged"]["bytes_mean_len_ge_4096"], *lc_sizes})
+        also["read_floor"] = time_read_floor(ada, device, sizes)
+        also["graded"] = graded_points(call_us, line["config"]["step_bytes"], also["mha_sweep"], mc,
+                                       also["read_floor"])
+    for name, fn in (("shards", time_shards), ("s2pro_run", time_s2pro_run),
+                     ("full_capacity_vs_active_prefix", time_full_vs_active), ("minicpm_sweep", time_minicpm_sweep),
+                     ("rope_step", time_rope_step), ("prefill", time_prefill)):
+        if name in wanted:
+            also[name] = fn(ada, device)
+    if not args.no_cpu_baseline and not args.long_context_only:
+        line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)
     return 0
 

@@ -465,6 +465,23 @@ int ada_step_graph_launch(ada_step_graph* graph, void* stream);
  * synchronise the streams it was launched on first. */
 void ada_step_graph_destroy(ada_step_graph* graph);
 
+/*
+ * Measurement: a plain streaming read, the floor a decode call's K/V stream
+ * is measured against. [DECODE-FASTPATH] "Current limitation" puts the whole
+ * cost of a one-token decode in reading K and V once; this reads `bytes`
+ * bytes of `src` once, with the 16-byte nontemporal loads the decode kernel
+ * uses and no arithmetic, spread over `workgroups` 256-thread workgroups
+ * (chunk i of 16 bytes to workgroup (i / 256) mod workgroups), and writes
+ * the xor of what each wavefront read to sink[4 * workgroup + wavefront]
+ * (so that no load can be dropped). Time it with events on `stream`.
+ *
+ *   src     device, 16-byte aligned, `bytes` (a multiple of 16) readable.
+ *   sink    device uint32 [4 * workgroups], 4-byte aligned, overwritten.
+ * ADA_ERR_SHAPE for workgroups outside 1..2^20 or bytes not a multiple of
+ * 16; ADA_OK without work for bytes == 0. One kernel launch.
+ */
+int ada_hbm_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

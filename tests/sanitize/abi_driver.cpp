@@ -129,6 +129,9 @@ int main() {
       if (s == ADA_OK) expect(ps >= 1 && ps <= ADA_MAX_SPLITS && pc >= 1, true, "fuzz plan range");
     }
     (void)ada_decode_workspace_bytes(B, Hq, Hkv, D, splits);
+    s = ada_hbm_read(ptr(), static_cast<size_t>(n) * 16 + (rng() % 4 == 0 ? 8 : 0), static_cast<uint32_t*>(ptr()),
+                     pick(), nullptr);
+    expect(known_status(s), true, "fuzz read probe");
     (void)ada_prefill_rows_per_workgroup(B, Hq, Hkv, n, pick());
     ada_step_layer layers[2];
     for (ada_step_layer& l : layers) l = {ptr(), ptr(), ptr(), ptr(), ptr(), ptr(), (rng() % 2) ? ptr() : nullptr, nullptr};

@@ -69,4 +69,9 @@ hipError_t launch_advance_positions(int32_t* pos, int batch, int, hipStream_t) {
   return hipSuccess;
 }
 
+hipError_t launch_hbm_read(const void* src, size_t bytes, uint32_t* sink, int workgroups, hipStream_t) {
+  require(src && sink && bytes > 0 && bytes % 16 == 0 && workgroups > 0, "read probe arguments");
+  return hipSuccess;
+}
+
 }  // namespace ada

@@ -366,3 +366,15 @@ def test_decode_plan_export(ada):
     assert f(1, 32, 8, 100, 0, 256, ctypes.byref(one), None) == -1
     assert f(1, 32, 8, 100, -1, 256, ctypes.byref(one), ctypes.byref(one)) == -8
     assert f(1, 32, 8, 100, 257, 256, ctypes.byref(one), ctypes.byref(one)) == -8
+
+
+def test_hbm_read_validation(ada):
+    f = ada._lib.ada_hbm_read
+    assert f(P, 1 << 20, P2, 0, NUL) == -2          # no workgroup
+    assert f(P, 1 << 20, P2, (1 << 20) + 1, NUL) == -2
+    assert f(P, (1 << 20) + 8, P2, 256, NUL) == -2  # not whole 16-byte chunks
+    assert f(NUL, 1 << 20, P2, 256, NUL) == -1
+    assert f(P, 1 << 20, NUL, 256, NUL) == -1
+    assert f(MIS, 1 << 20, P2, 256, NUL) == -9
+    assert f(P, 1 << 20, ctypes.c_void_p(0x20002), 256, NUL) == -9
+    assert f(NUL, 0, NUL, 256, NUL) == 0           # nothing to read
