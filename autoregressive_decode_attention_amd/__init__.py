@@ -11,6 +11,7 @@ The functions keep the C names without the ``ada_`` prefix:
 * ``kv_append(k_new, v_new, k_cache, v_cache, pos)``
 * ``decode_attn_gqa(q, k_cache, v_cache, kv_len, scale=None, out=None, max_kv_len=None)``
 * ``decode_attn_gqa_ex(..., num_splits=...)``
+* ``decode_attn_gqa_noalloc(...)``: the same with the library's static scratch (no allocation)
 * ``decode_step(q, k_new, v_new, k_cache, v_cache, pos, ...)``: append + decode in one call
 * ``decode_step_rope(q, k_new, v_new, cos, sin, k_cache, v_cache, pos, ...)`` and
   ``rope_kv_append(q, k_new, v_new, cos, sin, k_cache, v_cache, pos)``: the same
@@ -47,7 +48,7 @@ MAX_SPLITS = 256
 STATUS = {
     0: "ADA_OK", -1: "ADA_ERR_NULL", -2: "ADA_ERR_SHAPE", -3: "ADA_ERR_GQA", -4: "ADA_ERR_DTYPE",
     -5: "ADA_ERR_HEAD_DIM", -6: "ADA_ERR_SCALE", -7: "ADA_ERR_WORKSPACE", -8: "ADA_ERR_SPLITS",
-    -9: "ADA_ERR_ALIGN", -10: "ADA_ERR_HIP", -11: "ADA_ERR_DEVICE",
+    -9: "ADA_ERR_ALIGN", -10: "ADA_ERR_HIP", -11: "ADA_ERR_DEVICE", -12: "ADA_ERR_SCRATCH",
 }
 
 EXPORTS = (
@@ -56,7 +57,7 @@ EXPORTS = (
     "ada_decode_attn_gqa", "ada_decode_attn_gqa_ex", "ada_decode_partial", "ada_decode_combine",
     "ada_decode_step", "ada_rope_kv_append", "ada_decode_step_rope", "ada_prefill_append",
     "ada_prefill_attn_gqa", "ada_prefill_rows_per_workgroup", "ada_step_graph_create", "ada_step_graph_launch", "ada_step_graph_destroy",
-    "ada_hbm_read",
+    "ada_hbm_read", "ada_decode_attn_gqa_noalloc",
 )
 
 
@@ -92,6 +93,8 @@ def _declare(lib):
         "ada_decode_workspace_bytes": ([c_int, c_int, c_int, c_int, c_int], c_size_t),
         "ada_decode_attn_gqa": (decode_args, c_int),
         "ada_decode_attn_gqa_ex": (decode_args + [c_int], c_int),
+        "ada_decode_attn_gqa_noalloc": ([c_void_p] * 4 + [c_int] * 6 + [c_float, c_int, c_void_p, c_void_p, c_int],
+                                        c_int),
         "ada_decode_partial": ([c_void_p, c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
                                 c_float, c_int, c_int, c_void_p, c_size_t, ctypes.POINTER(c_int), c_void_p], c_int),
         "ada_decode_combine": ([c_void_p, c_size_t, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, c_void_p],
@@ -628,6 +631,29 @@ def hbm_read(src: torch.Tensor, sink: torch.Tensor, workgroups: int) -> None:
            "ada_hbm_read")
 
 
+def decode_attn_gqa_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len,
+                            scale: float | None = None, out: torch.Tensor | None = None,
+                            max_kv_len: int | None = None, num_splits: int = 0) -> torch.Tensor:
+    """``decode_attn_gqa_ex`` through ``ada_decode_attn_gqa_noalloc``: the split
+    partials go to the library's static per-device scratch buffer, so the call
+    allocates no device memory (``out`` must then be given by a caller that
+    cannot allocate; host lengths are still copied to the device here, so such
+    a caller passes an int32 GPU tensor or one host length). Calls on one
+    device must not overlap (they share the buffer)."""
+    B, Hq, Hkv, S, D = _check_decode_inputs(q, k_cache, v_cache)
+    if out is None:
+        out = torch.empty_like(q)
+    _require(out.shape == q.shape and out.dtype == q.dtype and out.device == q.device and out.is_contiguous(),
+             "out must be a contiguous tensor like q")
+    lens_t, mkl = _lengths(kv_len, max_kv_len, B, S, k_cache.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    _check(_lib.ada_decode_attn_gqa_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens_t), B, Hq, Hkv, D, S,
+                                            mkl, ctypes.c_float(scale), _DTYPE_CODES[k_cache.dtype], _ptr(out),
+                                            ctypes.c_void_p(_stream(k_cache.device)), int(num_splits)),
+           "ada_decode_attn_gqa_noalloc")
+    return out
+
+
 def decode_attn_gqa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_len,
                     scale: float | None = None, out: torch.Tensor | None = None,
                     max_kv_len: int | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
@@ -643,7 +669,7 @@ def decode_attn_gqa(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
 
 __all__ = [
     "AdaError", "F16", "BF16", "HEAD_DIM", "MAX_SPLITS", "EXPORTS", "LIB_PATH", "load_library",
-    "kv_append", "decode_attn_gqa", "decode_attn_gqa_ex", "decode_partial", "decode_combine", "decode_step", "decode_step_rope",
+    "kv_append", "decode_attn_gqa", "decode_attn_gqa_ex", "decode_attn_gqa_noalloc", "decode_partial", "decode_combine", "decode_step", "decode_step_rope",
     "rope_kv_append", "prefill_append", "prefill_attn_gqa", "decode_num_splits", "decode_plan", "decode_workspace_bytes",
     "new_workspace", "workspace_layout", "device_num_cus", "status_string", "last_hip_error",
     "abi_version", "StepGraph", "StepLayer", "step_graph", "prefill_rows_per_workgroup", "hbm_read",

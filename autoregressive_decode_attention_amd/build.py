@@ -17,7 +17,7 @@ CSRC = PKG_DIR / "csrc"
 INCLUDE = ROOT / "include"
 LIBRARY = PKG_DIR / "libada.so"
 SOURCES = [CSRC / "ada_kernels.hip", CSRC / "ada_prefill.hip", CSRC / "ada_graph.hip", CSRC / "ada_measure.hip",
-           CSRC / "ada_api.cpp"]
+           CSRC / "ada_noalloc.hip", CSRC / "ada_api.cpp"]
 ARCH = os.environ.get("ADA_OFFLOAD_ARCH", "gfx950")
 
 

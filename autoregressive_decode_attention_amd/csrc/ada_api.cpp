@@ -139,6 +139,7 @@ const char* ada_status_string(int status) {
     case ADA_ERR_ALIGN: return "device pointers must be 16-byte aligned";
     case ADA_ERR_HIP: return "HIP runtime error (see ada_last_hip_error)";
     case ADA_ERR_DEVICE: return "step graph launched on another device than the one it was created on";
+    case ADA_ERR_SCRATCH: return "the call needs more split scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -336,6 +337,28 @@ int ada_decode_attn_gqa(const void* q, const void* k_cache, const void* v_cache,
   return ada_decode_attn_gqa_ex(q, k_cache, v_cache, kv_len, batch, n_head, n_kv_head, head_dim,
                                 capacity, max_kv_len, scale, dtype, out, workspace,
                                 workspace_bytes, stream, 0);
+}
+
+int ada_decode_attn_gqa_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_len,
+                                int batch, int n_head, int n_kv_head, int head_dim, int capacity, int max_kv_len,
+                                float scale, int dtype, void* out, void* stream, int num_splits) {
+  ada::DecodeLaunch p{};
+  int rc = prepare_decode(q, k_cache, v_cache, kv_len, batch, n_head, n_kv_head, head_dim, capacity,
+                          max_kv_len, scale, dtype, num_splits, stream, &p);
+  if (rc != ADA_OK || batch == 0) return rc;
+  if (!out) return ADA_ERR_NULL;
+  if (!aligned16(out)) return ADA_ERR_ALIGN;
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  if (p.splits > 1) {
+    if (ada::workspace_layout(batch, n_head, n_kv_head, ada::kHeadDim, p.splits).total > ada::kScratchBytes)
+      return ADA_ERR_SCRATCH;
+    hipError_t e = ada::scratch_buffer(&scratch);
+    if (e != hipSuccess) return hip_fail(e);
+    scratch_bytes = ada::kScratchBytes;
+  }
+  return ada_decode_attn_gqa_ex(q, k_cache, v_cache, kv_len, batch, n_head, n_kv_head, head_dim, capacity,
+                                max_kv_len, scale, dtype, out, scratch, scratch_bytes, stream, num_splits);
 }
 
 }  // extern "C"

@@ -13,6 +13,9 @@ constexpr int kMaxGroup = 8;
 constexpr int kThreads = 256;    // 4 wavefronts of 64
 constexpr int kTileRows = 64;    // slot granularity the heuristic rounds split ranges to
 constexpr int kMaxSplits = 256;  // equals ADA_MAX_SPLITS
+// Bytes of the static per-device scratch buffer of the allocation-free
+// decode entry point (equals ADA_NOALLOC_SCRATCH_BYTES).
+constexpr size_t kScratchBytes = size_t(4) << 20;
 
 // Workspace layout for `splits` splits, split-major (the partials of one
 // split are contiguous, so partials computed on separate key ranges can be
@@ -100,6 +103,10 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache,
                             hipStream_t stream);
 
 hipError_t launch_advance_positions(int32_t* pos, int batch, int delta, hipStream_t stream);
+
+// Device address of the current device's static scratch buffer
+// (kScratchBytes, 256-byte aligned), fetched once per device.
+hipError_t scratch_buffer(void** ptr);
 
 // Streaming read of `bytes` (a multiple of 16) from src by `workgroups`
 // 256-thread workgroups; one 32-bit xor per wavefront to sink.

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define ADA_ABI_VERSION 2
+#define ADA_ABI_VERSION 3
 
 /* Element type of q, caches, new rows and output. */
 typedef enum ada_dtype { ADA_F16 = 0, ADA_BF16 = 1 } ada_dtype;
@@ -65,8 +65,10 @@ typedef enum ada_status {
   ADA_ERR_SPLITS = -8,    /* num_splits outside [0, ADA_MAX_SPLITS]           */
   ADA_ERR_ALIGN = -9,     /* a device pointer is not 16-byte aligned          */
   ADA_ERR_HIP = -10,      /* a HIP runtime call failed                        */
-  ADA_ERR_DEVICE = -11    /* a step graph launched on another device than the
+  ADA_ERR_DEVICE = -11,   /* a step graph launched on another device than the
                              one current when it was created                 */
+  ADA_ERR_SCRATCH = -12   /* ada_decode_attn_gqa_noalloc: the call's split
+                             partials exceed ADA_NOALLOC_SCRATCH_BYTES        */
 } ada_status;
 
 /* Upper bound on the number of key-range splits of one decode call. */
@@ -245,6 +247,33 @@ int ada_decode_attn_gqa_ex(const void* q, const void* k_cache, const void* v_cac
                            int head_dim, int capacity, int max_kv_len, float scale, int dtype,
                            void* out, void* workspace, size_t workspace_bytes, void* stream,
                            int num_splits);
+
+/*
+ * ada_decode_attn_gqa_ex without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. The split partials go to a static
+ * scratch array of ADA_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * device it runs on until the process ends; the call allocates nothing
+ * (no hipMalloc, no hipFree). Same kernels, plan and results as
+ * ada_decode_attn_gqa_ex with the same num_splits (0 = heuristic).
+ *
+ * Limit: ADA_ERR_SCRATCH when the call uses two or more splits and
+ * ada_decode_workspace_bytes(batch, n_head, n_kv_head, head_dim, splits)
+ * exceeds ADA_NOALLOC_SCRATCH_BYTES (about 8000 (batch row, query head,
+ * split) partials: e.g. batch 8 x 32 heads x 8 splits uses 1.06 MB).
+ * The scratch array is shared by every call on a device and keeps the last
+ * call's contents (nothing in it needs clearing: each call writes every
+ * partial it reads). Calls that may overlap on one device -- on different
+ * streams without synchronisation, or from several threads -- race on it;
+ * order them. The first call on a device fetches the array's address
+ * (hipGetSymbolAddress), so it is ADA_ERR_HIP if that fails.
+ */
+#define ADA_NOALLOC_SCRATCH_BYTES (4u << 20)
+
+int ada_decode_attn_gqa_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* kv_len, int batch, int n_head, int n_kv_head,
+                                int head_dim, int capacity, int max_kv_len, float scale, int dtype,
+                                void* out, void* stream, int num_splits);
 
 /*
  * One whole decode step in one call: append the new key/value rows, then

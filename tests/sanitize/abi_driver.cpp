@@ -22,7 +22,7 @@ void expect(int got, int want, const char* what) {
     ++failures;
   }
 }
-bool known_status(int s) { return s <= 0 && s >= -11; }
+bool known_status(int s) { return s <= 0 && s >= -12; }
 void* dev(uintptr_t k) { return reinterpret_cast<void*>(0x100000 + 256 * k); }
 int32_t* dev_i(uintptr_t k) { return static_cast<int32_t*>(dev(k)); }
 void* misaligned() { return reinterpret_cast<void*>(0x100008); }
@@ -129,6 +129,9 @@ int main() {
       if (s == ADA_OK) expect(ps >= 1 && ps <= ADA_MAX_SPLITS && pc >= 1, true, "fuzz plan range");
     }
     (void)ada_decode_workspace_bytes(B, Hq, Hkv, D, splits);
+    s = ada_decode_attn_gqa_noalloc(ptr(), ptr(), ptr(), static_cast<const int32_t*>(ptr()), B, Hq, Hkv, D, S, n,
+                                    sc, dt, ptr(), nullptr, splits);
+    expect(known_status(s), true, "fuzz noalloc");
     s = ada_hbm_read(ptr(), static_cast<size_t>(n) * 16 + (rng() % 4 == 0 ? 8 : 0), static_cast<uint32_t*>(ptr()),
                      pick(), nullptr);
     expect(known_status(s), true, "fuzz read probe");

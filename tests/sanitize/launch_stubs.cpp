@@ -5,6 +5,7 @@
 // built against what every launch must satisfy and aborts otherwise (the
 // sanitizer run then fails).
 #include <cstdio>
+#include <cstdint>
 #include <cstdlib>
 
 #include "ada_internal.h"
@@ -66,6 +67,12 @@ hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_cache,
 
 hipError_t launch_advance_positions(int32_t* pos, int batch, int, hipStream_t) {
   require(pos && batch > 0, "advance arguments");
+  return hipSuccess;
+}
+
+// Stand-in for the static scratch buffer: a fixed, never dereferenced address.
+hipError_t scratch_buffer(void** ptr) {
+  *ptr = reinterpret_cast<void*>(uintptr_t{0x7f0000000000});
   return hipSuccess;
 }
 

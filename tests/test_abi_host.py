@@ -47,8 +47,8 @@ def test_library_exports_every_declared_symbol(ada):
 
 
 def test_abi_version_and_status_strings(ada):
-    assert ada.abi_version() == 2
-    for code in range(-11, 1):
+    assert ada.abi_version() == 3
+    for code in range(-12, 1):
         assert ada.status_string(code) and ada.status_string(code) != "unknown status"
     assert ada.status_string(-99) == "unknown status"
 
@@ -378,3 +378,33 @@ def test_hbm_read_validation(ada):
     assert f(MIS, 1 << 20, P2, 256, NUL) == -9
     assert f(P, 1 << 20, ctypes.c_void_p(0x20002), 256, NUL) == -9
     assert f(NUL, 0, NUL, 256, NUL) == 0           # nothing to read
+
+
+def test_noalloc_validation(ada):
+    """ada_decode_attn_gqa_noalloc: the decode checks, then the limit of the
+    static scratch (forced split counts need no device, so this runs on the
+    CPU); a call over the limit is rejected before any HIP call."""
+    f = ada._lib.ada_decode_attn_gqa_noalloc
+    sc = ctypes.c_float(0.088)
+
+    def call(B=1, Hq=32, Hkv=8, D=128, S=4096, n=4096, dtype=1, out=P4, splits=8, q=P):
+        return f(q, P2, P3, NUL, B, Hq, Hkv, D, S, n, sc, dtype, out, NUL, splits)
+
+    assert call(dtype=7) == -4
+    assert call(D=64) == -5
+    assert call(Hq=36) == -3
+    assert call(out=NUL) == -1
+    assert call(q=NUL) == -1
+    assert call(out=MIS) == -9
+    assert call(splits=300) == -8
+    assert call(n=5000) == -2
+    assert call(B=0, q=NUL, out=NUL) == 0
+    limit = 4 << 20
+    # 64 rows x 64 heads x 256 splits of partials: far beyond the scratch
+    assert ada.decode_workspace_bytes(64, 64, 8, 128, 256) > limit
+    assert call(B=64, Hq=64, S=1 << 16, n=1 << 16, splits=256) == -12
+    # the largest forced count that fits for batch 8 x 32 heads (the long-context shape) is checked exactly
+    fits = max(s for s in range(1, 257) if ada.decode_workspace_bytes(8, 32, 8, 128, s) <= limit)
+    assert ada.decode_workspace_bytes(8, 32, 8, 128, fits + 1) > limit
+    assert call(B=8, S=32768, n=32768, splits=fits + 1) == -12
+    assert ada.status_string(-12) != "unknown status"
