@@ -79,11 +79,11 @@ Plan forced_plan(int max_kv_len, int requested) {
 }
 
 // Heuristic (measured on MI355X, cold HBM): one 4-wave workgroup per compute
-// unit for grouped heads (G >= 2: their key-row work keeps the SIMDs busy),
-// two for G == 1; splits never shorter than 64 slots (one workgroup tile);
-// while a split would exceed 4096 slots, double the split count so long rows
-// still spread over every compute unit. Ranges are rounded up to whole
-// 64-slot tiles.
+// unit (a streaming read on this device is fastest with one workgroup per
+// compute unit, and two per unit only add partials); splits never shorter
+// than 64 slots (one workgroup tile); while a split would exceed 8192 slots,
+// double the split count so long rows still spread over every compute unit.
+// Ranges are rounded up to whole 64-slot tiles.
 Plan heuristic_plan(int batch, int n_head, int n_kv_head, int max_kv_len, int num_cus) {
   if (batch <= 0 || n_head <= 0 || n_kv_head <= 0 || max_kv_len <= 0 || num_cus <= 0)
     return {1, max_kv_len > 0 ? max_kv_len : 1};
@@ -93,12 +93,11 @@ Plan heuristic_plan(int batch, int n_head, int n_kv_head, int max_kv_len, int nu
   if (max_kv_len <= 4 * ada::kTileRows)
     return {1, static_cast<int>(ceil_div(max_kv_len, ada::kTileRows) * ada::kTileRows)};
   const int64_t units = static_cast<int64_t>(batch) * n_kv_head;
-  const int64_t per_cu = n_head == n_kv_head ? 2 : 1;
-  int64_t splits = ceil_div(per_cu * num_cus, units);
+  int64_t splits = ceil_div(num_cus, units);
   const int64_t by_len = ceil_div(max_kv_len, ada::kTileRows);
   if (splits > by_len) splits = by_len;
   if (splits < 1) splits = 1;
-  while (ceil_div(max_kv_len, splits) > 4096 && splits * 2 <= by_len) splits *= 2;
+  while (ceil_div(max_kv_len, splits) > 8192 && splits * 2 <= by_len) splits *= 2;
   if (splits > ADA_MAX_SPLITS) splits = ADA_MAX_SPLITS;
   int64_t chunk = ceil_div(ceil_div(max_kv_len, splits), ada::kTileRows) * ada::kTileRows;
   return {static_cast<int>(ceil_div(max_kv_len, chunk)), static_cast<int>(chunk)};

@@ -146,9 +146,8 @@ int ada_rope_kv_append(const void* q, void* q_out, const void* k_new, const void
  * batch * n_kv_head (batch row, KV head) units whose live prefixes are at
  * most max_kv_len slots, on a device with num_cus compute units. Prefixes of
  * at most 256 slots take one split (no combine launch). Otherwise it aims at
- * one 4-wave workgroup per compute unit when query heads are grouped
- * (n_head > n_kv_head) and two otherwise, never splits below 64 slots, and
- * doubles the split count while a split would exceed 4096 slots; the
+ * one 4-wave workgroup per compute unit, never splits below 64 slots, and
+ * doubles the split count while a split would exceed 8192 slots; the
  * per-split range is rounded up to a multiple of 64 and the count returned
  * is the one that rounding yields. Pure host arithmetic; returns 1..256
  * (1 for non-positive inputs).

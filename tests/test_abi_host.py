@@ -312,9 +312,10 @@ def test_workspace_bytes_arithmetic(ada):
 def test_split_heuristic_properties(ada):
     ns = ada.decode_num_splits
     # worked examples on a 256-CU device (the values the tuning sweeps favoured)
-    assert ns(8, 32, 8, 32768, 256) == 8     # long context: 4 splits would be 8192 slots -> doubled
-    assert ns(1, 16, 16, 4096, 256) == 32    # MHA kv 4096: two workgroups per CU, 128-slot splits
-    assert ns(1, 16, 16, 8192, 256) == 32
+    assert ns(8, 32, 8, 32768, 256) == 4     # long context: one workgroup per CU, 8192-slot splits
+    assert ns(1, 16, 16, 4096, 256) == 16    # MHA kv 4096: one workgroup per CU, 256-slot splits
+    assert ns(1, 16, 16, 8192, 256) == 16
+    assert ns(8, 32, 8, 65536, 256) == 8     # 16384-slot splits would exceed 8192 -> doubled
     assert ns(1, 16, 16, 1024, 256) == 16    # capped by 64-slot splits
     assert ns(4, 32, 8, 8192, 256) == 8      # MiniCPM shape: one workgroup per CU
     assert ns(1, 32, 8, 400, 256) == 7       # tiny
@@ -331,12 +332,12 @@ def test_split_heuristic_properties(ada):
                 # the count is the one the 64-slot rounding yields, and every split is live
                 assert s == -(-n // chunk)
                 assert s <= max(1, -(-n // 64))
-                # splits longer than 4096 slots only when the split count is at its cap
-                if chunk > 4096 + 63:
+                # splits longer than 8192 slots only when the split count is at its cap
+                if chunk > 8192 + 63:
                     assert s * 2 > -(-n // 64) or s * 2 > 256
-                # splitting never asks for more than two workgroups per CU unless rows are long
-                if s > 1 and B * Hkv * s > 2 * 256:
-                    assert chunk >= 2048
+                # splitting never asks for more than one workgroup per CU unless rows are long
+                if s > 1 and B * Hkv * s > 256:
+                    assert chunk > 4096 - 64
     assert ns(0, 8, 8, 100, 256) == 1
     assert ns(1, 8, 8, 0, 256) == 1
     assert ns(1, 8, 8, 100, 0) == 1
@@ -357,8 +358,8 @@ def test_decode_plan_export(ada):
             for forced in (1, 2, 3, 7, 40, 256):
                 s, c = plan(B, Hq, Hkv, n, forced)
                 assert c == -(-n // forced) and s == -(-n // c) and s <= forced
-    assert plan(8, 32, 8, 32768, 0) == (8, 4096)
-    assert plan(1, 16, 16, 4096, 0) == (32, 128)
+    assert plan(8, 32, 8, 32768, 0) == (4, 8192)
+    assert plan(1, 16, 16, 4096, 0) == (16, 256)
     assert plan(1, 32, 8, 0, 5) == (1, 1)
     f = ada._lib.ada_decode_plan
     one = ctypes.c_int(0)
