@@ -158,3 +158,30 @@ def test_minicpm_sweep_step_graph(ada, ora):
     shp = W.WORKLOADS["minicpm_stream"].shape
     S = shp.capacity
     run_graph_sweep(ada, ora, "MiniCPM step graph", shp, 4, 0, S, S - 1, {0, 1, 4095, S - 1}, (0, 3), 31_000)
+
+
+def test_minicpm_ragged_bench_draws(ada, ora):
+    """The 64 ragged MiniCPM draws bench.py times (per-row kv_len from the same
+    seeds, uniform in [1, 8192]; batch 4, 32/8 heads, bf16): the same call
+    with device lengths (the balanced plan) and the heuristic split count,
+    against the oracle. The cache is drawn once; each draw's GPU copy gets NaN
+    beyond every row's length, so a read past a live prefix shows."""
+    shp = W.WORKLOADS["minicpm_stream"].shape
+    B, S = shp.batch, shp.capacity
+    say(f"case MiniCPM ragged bench draws: B={B} {shp.n_head}/{shp.n_kv_head} {shp.dtype} S={S}, 64 draws")
+    x = W.decode_inputs(shp, [S] * B, W.seed_for(3, 70_000), tail="random")
+    q, kc, vc = x["q"].cuda(), x["k_cache"].cuda(), x["v_cache"].cuda()
+    splits, _ = ada.decode_plan(B, shp.n_head, shp.n_kv_head, S)
+    ws = ada.new_workspace(ada.decode_workspace_bytes(B, shp.n_head, shp.n_kv_head, 128, max(2, splits)), "cuda")
+    out = torch.empty_like(q)
+    for d in range(64):
+        lens = W.ragged_lengths(B, 1, S, W.seed_for(3, 72_000 + d))
+        k_d, v_d = kc.clone(), vc.clone()
+        for b, n in enumerate(lens):
+            k_d[b, :, n:] = float("nan")
+            v_d[b, :, n:] = float("nan")
+        lt = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        ada.decode_attn_gqa(q, k_d, v_d, lt, scale=SCALE, out=out, max_kv_len=S, workspace=ws)
+        torch.cuda.synchronize()
+        want = ora.decode(x["q"], x["k_cache"], x["v_cache"], lens, SCALE)
+        assert_parity(out, want, shp.dtype, f"ragged bench draw {d} lens={lens}")
